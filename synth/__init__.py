@@ -5,8 +5,10 @@ This module holds generators only: it writes quant blocks directly as bytes
 vectors and expert ids.  It decodes nothing, multiplies nothing and holds no
 table of the formats' values, so it carries none of the GEMV's arithmetic.
 
-Every generator is a pure function of its seed (numpy ``Generator(PCG64)``).
-Seeds follow ``1000 * cfg + tensor_id`` for the five workloads below.
+Every generator is a pure function of its seed: quant blocks come from the
+counter-based generator in ``synth.c`` (SplitMix64 output function, built with
+gcc), activations and expert ids from numpy ``Generator(PCG64)``.  Seeds
+follow ``1000 * cfg + tensor_id`` for the five workloads below.
 
 Block layouts written here (byte order little-endian):
   Q8_0  (34 B): fp16 scale bits, then 32 int8 codes
@@ -14,6 +16,10 @@ Block layouts written here (byte order little-endian):
   MXFP4 (17 B): E8M0 scale byte, then 16 bytes of packed 4-bit codes
 """
 from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
 
 import numpy as np
 
@@ -26,65 +32,71 @@ def rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
 
 
-CHUNK_ROWS = 256  # rows per independently seeded chunk
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+_lib = None
 
 
-def _fp16_scale_bits(g: np.random.Generator, n: int, lo: float, hi: float, random_sign: bool) -> np.ndarray:
-    """Scales drawn as doubles in [lo, hi), rounded once to binary16 (round to
-    nearest even, numpy's cast), optionally given a uniform random sign.
-    Returned as the raw 16-bit patterns."""
-    u = g.random(n)
-    d = (lo + (hi - lo) * u).astype(np.float16)
-    if random_sign:
-        neg = g.integers(0, 2, size=n).astype(bool)
-        d = np.where(neg, -d, d).astype(np.float16)
-    return d.view(np.uint16)
+def build() -> str:
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
 
 
-def _chunk(fmt: int, rows: int, k: int, g: np.random.Generator, p: dict) -> np.ndarray:
-    """One chunk of rows: all code bytes first (drawn over the whole block so
-    that the scale bytes are overwritten afterwards), then the scales."""
-    bb = BLOCK_BYTES[fmt]
-    nb = rows * (k // 32)
-    if fmt == Q8_0:
-        out = g.integers(-127, 128, size=nb * bb, dtype=np.int8).view(np.uint8).reshape(nb, bb)
-        out[:, 0:2] = _fp16_scale_bits(g, nb, p.get("scale_lo", 1e-3), p.get("scale_hi", 1e-2),
-                                       p.get("random_sign", True)).view(np.uint8).reshape(nb, 2)
-    elif fmt == Q4_0:
-        out = g.integers(0, 256, size=nb * bb, dtype=np.uint8).reshape(nb, bb)
-        out[:, 0:2] = _fp16_scale_bits(g, nb, p.get("scale_lo", 1e-3), p.get("scale_hi", 1e-2),
-                                       p.get("random_sign", False)).view(np.uint8).reshape(nb, 2)
-    elif fmt == MXFP4:
-        out = g.integers(0, 256, size=nb * bb, dtype=np.uint8).reshape(nb, bb)
-        out[:, 0] = g.integers(p.get("e_lo", 118), p.get("e_hi", 130) + 1, size=nb, dtype=np.uint8)
-    else:
-        raise ValueError(f"unknown format {fmt}")
-    return out.reshape(rows, (k // 32) * bb)
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.synth_fill.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_uint64, ctypes.c_double, ctypes.c_double, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_int32]
+        L.synth_fill.restype = ctypes.c_int
+        L.synth_word.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64]
+        L.synth_word.restype = ctypes.c_uint64
+        L.synth_half_bits.argtypes = [ctypes.c_double]
+        L.synth_half_bits.restype = ctypes.c_uint16
+        _lib = L
+    return _lib
 
 
-def blocks(fmt: int, n_rows: int, k: int, seed: int, r0: int = 0, r1: int | None = None, **p) -> np.ndarray:
-    """Rows [r0, r1) of a seeded (n_rows, k/32 * block_bytes) uint8 matrix.
+DEFAULTS = {
+    Q8_0: dict(scale_lo=1e-3, scale_hi=1e-2, random_sign=True),
+    Q4_0: dict(scale_lo=1e-3, scale_hi=1e-2, random_sign=False),
+    MXFP4: dict(e_lo=118, e_hi=130),
+}
 
-    Rows come in chunks of CHUNK_ROWS, chunk c drawn from
-    PCG64(SeedSequence([seed, c])), so any row range can be regenerated
-    without the rest of the matrix.  Distributions:
+
+def blocks(fmt: int, n_rows: int, k: int, seed: int, r0: int = 0, r1: int | None = None, out=None,
+           threads: int | None = None, **p) -> np.ndarray:
+    """Rows [r0, r1) of the seeded (n_rows, k/32 * block_bytes) uint8 matrix.
+
+    Every block is drawn from its own counter range (synth.c), so a row range
+    can be regenerated alone and the bytes do not depend on the thread count.
       Q8_0 : d ~ fp16(U[1e-3, 1e-2)) * (+-1), q ~ U{-127..127}
       Q4_0 : d ~ fp16(U[1e-3, 1e-2)), every code byte ~ U{0..255}
       MXFP4: e ~ U{118..130}, every code byte ~ U{0..255}
+    ``out`` (optional) is a C-contiguous uint8 array of the result's shape.
     """
     assert k % 32 == 0 and k > 0
     r1 = n_rows if r1 is None else r1
     assert 0 <= r0 <= r1 <= n_rows
+    q = dict(DEFAULTS[fmt])
+    q.update(p)
     rb = (k // 32) * BLOCK_BYTES[fmt]
-    out = np.empty((r1 - r0, rb), dtype=np.uint8)
-    c0, c1 = r0 // CHUNK_ROWS, (r1 + CHUNK_ROWS - 1) // CHUNK_ROWS
-    for c in range(c0, c1):
-        lo, hi = c * CHUNK_ROWS, min((c + 1) * CHUNK_ROWS, n_rows)
-        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, c])))
-        ch = _chunk(fmt, hi - lo, k, g, p)
-        a, b = max(lo, r0), min(hi, r1)
-        out[a - r0:b - r0] = ch[a - lo:b - lo]
-    return out
+    if out is None:
+        out = np.empty((r1 - r0, rb), dtype=np.uint8)
+    assert out.dtype == np.uint8 and out.flags.c_contiguous and out.size == (r1 - r0) * rb
+    t = threads or int(os.environ.get("OMP_NUM_THREADS", 0) or (os.cpu_count() or 1))
+    rc = _load().synth_fill(fmt, out.ctypes.data, k, r0, r1, seed & (2 ** 64 - 1), float(q.get("scale_lo", 1e-3)),
+                            float(q.get("scale_hi", 1e-2)), int(bool(q.get("random_sign", False))),
+                            int(q.get("e_lo", 118)), int(q.get("e_hi", 130)), min(t, 64))
+    if rc != 0:
+        raise ValueError("synth_fill rejected the arguments")
+    return out.reshape(r1 - r0, rb)
 
 
 def q8_0_blocks(n_rows, k, seed, **p):
