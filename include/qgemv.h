@@ -1,0 +1,208 @@
+/*
+ * qgemv.h -- C ABI of libqgemv.so: batch-1 dequant-GEMV over GGUF
+ * block-quantized weights (Q8_0, Q4_0, MXFP4) on an AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (RAMforge README, "Milestone 6 - True Out-of-Core Integrity",
+ * matrix layout): a weight matrix of n_rows output rows and k inputs is stored
+ * row-major, [n_rows][k/32 blocks], each row a whole number of 32-weight quant
+ * blocks (neurostream README, "The idea"), and
+ *
+ *     y[j] = sum_{i<k} W[row_start + j, i] * x[i],   0 <= j < row_end - row_start
+ *
+ * with every block dequantized in registers and never written out, fp32
+ * activations and fp32 accumulation.
+ *
+ * Block formats (RAMforge README, "Milestone 5 - Native Quantized Tensor
+ * Support"; MXFP4 from neurostream README, "The idea", 4.41 MB per 2,880 x 2,880
+ * expert = 17 bytes per 32 weights):
+ *   QG_Q8_0  34 B: fp16 d, int8 q[32];              w_j = d * q_j
+ *   QG_Q4_0  18 B: fp16 d, uint8 qs[16];            w_j = d * (nib_j - 8)
+ *   QG_MXFP4 17 B: uint8 e (E8M0), uint8 qs[16];    w_j = 2^(e-127) * E2M1(nib_j)
+ * Nibble order: element j < 16 is the low nibble of qs[j], element j + 16 the
+ * high nibble (the GGUF split-half order).  E2M1 is the OCP MX 4-bit float
+ * (sign bit 3, two exponent bits with bias 1, one mantissa bit); e = 255 is NaN.
+ *
+ * Conventions shared by every entry point
+ *  - Status: 0 (QG_OK) or a negative qg_status.  Arguments are validated on the
+ *    host before any HIP call; a call that fails validation enqueues nothing and
+ *    leaves every output untouched (fail closed: hipfire PR, "Design notes").
+ *  - Memory: the caller owns every weight, activation and output buffer and
+ *    every stream.  Pointers marked "device" are device (HBM) addresses; the
+ *    streamed entry points take weights in page-locked host memory
+ *    (hipHostMalloc / pinned), checked, never pageable.
+ *  - Asynchrony: compute entry points enqueue on `stream` (NULL = the default
+ *    stream) and return without waiting.  Only qgemv_stream_create and
+ *    qgemv_stream_destroy synchronise.
+ *  - Outputs: y receives exactly row_end - row_start values; nothing outside
+ *    that range is written.
+ *  - Determinism: a row's result depends only on its own bytes, x, the format
+ *    and k.  It does not depend on the window, block_rows, the grid, the stream
+ *    or whether the weights were streamed, so all those give identical bits.
+ *  - Threads: stateless calls are re-entrant; a qg_streamer is not thread-safe.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t *qg_stream_t;
+
+enum qg_format { QG_Q8_0 = 1, QG_Q4_0 = 2, QG_MXFP4 = 3 };
+
+enum qg_status {
+  QG_OK = 0,
+  QG_E_NULL = -1,       /* a required pointer is NULL */
+  QG_E_FMT = -2,        /* unknown format (RAMforge README, "Capability registry":
+                           unsupported types are an explicit error) */
+  QG_E_SHAPE = -3,      /* k <= 0, k % 32 != 0, k > QG_MAX_K, n_rows < 0,
+                           n_expert <= 0, rows not a multiple of n_expert */
+  QG_E_RANGE = -4,      /* row_start < 0, row_start > row_end, row_end > n_rows,
+                           expert id outside [0, n_expert) */
+  QG_E_SIZE = -5,       /* n_bytes != n_rows * (k/32) * block bytes (truncated or
+                           oversized tensors are rejected: RAMforge README,
+                           "Build & Test", quant.rs unit tests) */
+  QG_E_ARG = -6,        /* block_rows < 0, lookahead < 1, n_win < 0 or above
+                           QG_MAX_WINDOWS, n < 0, bad eps, x_stride < 0 */
+  QG_E_NOT_PINNED = -7, /* streamed weights not in page-locked host memory */
+  QG_E_CAPACITY = -8,   /* a streamed row block is larger than a ring slot */
+  QG_E_HIP = -100       /* a HIP runtime call failed; see qgemv_last_hip_error */
+};
+
+/* Most windows one grid takes (the window table travels in kernel arguments). */
+#define QG_MAX_WINDOWS 64
+
+/* Largest k: a row's block columns are spread over at most 8 wavefronts with
+ * at most 4 columns per lane, each lane holding its activations in registers. */
+#define QG_MAX_K 65536
+
+/* A whole quantized weight matrix: the compact resident representation of a
+ * quantized tensor (RAMforge README, "Milestone 5", QuantizedTensor: raw block
+ * bytes plus type and shape). */
+typedef struct qg_matrix {
+  const void *data; /* n_bytes of blocks, row-major [n_rows][k/32] */
+  int32_t fmt;      /* enum qg_format */
+  int32_t reserved; /* must be 0 */
+  int64_t n_rows;   /* output rows */
+  int64_t k;        /* inputs per row, a multiple of 32 */
+  int64_t n_bytes;  /* must equal qgemv_weight_bytes(fmt, n_rows, k) */
+} qg_matrix;
+
+/* A row window of one matrix with its own activation and output vectors
+ * (neurostream README, "How it works", step 4: row_start/row_end bound the
+ * walk over a weight matrix).  All windows of one call share fmt and k. */
+typedef struct qg_window {
+  const void *data;  /* the matrix's row 0 (not the window's first row) */
+  int64_t n_rows;    /* rows of that matrix, for range checks */
+  int64_t row_start; /* first row of the window */
+  int64_t row_end;   /* one past the last row */
+  const float *x;    /* device, k values */
+  float *y;          /* device, row_end - row_start values: y[j] <-> row row_start + j */
+} qg_window;
+
+/* Bytes per 32-weight block: 34, 18 or 17; QG_E_FMT for an unknown format. */
+int64_t qgemv_block_bytes(int32_t fmt);
+
+/* Bytes of an n_rows x k matrix, or a negative status (QG_E_FMT, QG_E_SHAPE). */
+int64_t qgemv_weight_bytes(int32_t fmt, int64_t n_rows, int64_t k);
+
+/* y = W[row_start:row_end] . x, weights resident in device memory.
+ * w->data, x (k floats) and y (row_end - row_start floats) are device pointers.
+ * block_rows = B > 0 splits the window into row blocks
+ * [row_start + iB, min(row_start + (i+1)B, row_end)) (neurostream README,
+ * "The idea": --block-rows; 0 keeps the whole window as one block); all blocks
+ * are computed by one grid and the result does not depend on B. */
+int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
+               const float *x, float *y, int64_t block_rows, qg_stream_t stream);
+
+/* Several row windows (any matrices of the same fmt and k, each with its own
+ * x and y) computed by ONE grid.  win is a host array of n_win entries,
+ * 0 <= n_win <= QG_MAX_WINDOWS; n_win = 0 is a no-op. */
+int qgemv_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win,
+                  int64_t block_rows, qg_stream_t stream);
+
+/* Selected experts of stacked (n_expert, out, k) tensors (neurostream README,
+ * "The idea" and "How it works" step 2: expert e owns rows [e*out, (e+1)*out)
+ * and only router-named experts are read).  mats is a host array of n_mat
+ * matrices of the same fmt, k and n_rows = n_expert * out; ids is a host array
+ * of n_sel expert ids.  All n_mat * n_sel windows run in ONE grid.
+ * Input of selected expert s: x + s * x_stride (x_stride = 0: one shared x).
+ * Output of matrix m, selected expert s: y + (m * n_sel + s) * out.
+ * n_mat * n_sel must not exceed QG_MAX_WINDOWS. */
+int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert,
+                         const int32_t *ids, int32_t n_sel, const float *x,
+                         int64_t x_stride, float *y, int64_t block_rows,
+                         qg_stream_t stream);
+
+/* h[i] = silu(g[i]) * u[i], silu(v) = v / (1 + exp(-v)), fp32, device
+ * pointers, n >= 0 (the SwiGLU activation between the row-contiguous gate/up
+ * and down phases: neurostream README, "How it works"; run on the GPU as in
+ * hipfire PR, "Design notes", silu_mul). */
+int qgemv_silu_mul(const float *g, const float *u, float *h, int64_t n, qg_stream_t stream);
+
+/* out = rms(act(v)), act = identity (gelu = 0) or exact erf GELU (gelu = 1),
+ * rms(t) = t / sqrt(mean(t^2) + eps), no gain; fp32, device pointers, n >= 1,
+ * eps >= 0.  The activation carry between the GEMVs of the synthetic dense
+ * decode pass. */
+int qgemv_rms_carry(const float *v, float *out, int64_t n, float eps, int32_t gelu,
+                    qg_stream_t stream);
+
+/* Decoded fp32 weights of rows [row_start, row_end): out is device memory of
+ * (row_end - row_start) * k floats, row-major.  Uses the GEMV kernels' own
+ * block decoders; a test aid for the bit-exact decode check. */
+int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
+                       float *out, qg_stream_t stream);
+
+/* ---- streamed weights: pinned host memory -> device ring -> same kernels ----
+ * A streamer owns lookahead + 1 device slots of slot_bytes each, one copy
+ * stream and per-slot events (neurostream README, "The idea": blocks sized so
+ * that lookahead + 1 buffers fit; "Bugs worth knowing about": the pipeline
+ * holds depth + 1 blocks, because the block being multiplied keeps its
+ * buffer until its output exists).  Block k is copied on the copy stream into
+ * slot k mod (lookahead + 1) once the kernel of block k - lookahead - 1 has
+ * released that slot; its kernel runs on the caller's stream after the copy. */
+typedef struct qg_streamer qg_streamer;
+
+/* slot_bytes >= 1, lookahead >= 1.  Allocates (lookahead + 1) * slot_bytes of
+ * device memory.  Synchronising. */
+int qgemv_stream_create(int64_t slot_bytes, int32_t lookahead, qg_streamer **out);
+
+/* Device bytes the ring holds: (lookahead + 1) * slot_bytes; negative status on
+ * a NULL streamer. */
+int64_t qgemv_stream_ring_bytes(const qg_streamer *st);
+
+/* As qgemv_rows, with w->data in pinned host memory: the window is walked in
+ * row blocks of block_rows (0 = whole window), each copied into the ring and
+ * multiplied there.  Every block must fit one slot (else QG_E_CAPACITY).
+ * x and y are device pointers.  `stream` waits for the last block's kernel. */
+int qgemv_stream_rows(qg_streamer *st, const qg_matrix *w, int64_t row_start,
+                      int64_t row_end, int64_t block_rows, const float *x, float *y,
+                      qg_stream_t stream);
+
+/* As qgemv_windows, with every win[i].data in pinned host memory; the blocks
+ * of all windows go through the ring in window order. */
+int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win,
+                         int32_t n_win, int64_t block_rows, qg_stream_t stream);
+
+/* Waits for the streamer's work, frees it.  NULL is a no-op. */
+int qgemv_stream_destroy(qg_streamer *st);
+
+/* Static text for a status. */
+const char *qgemv_strerror(int status);
+
+/* Text of the last QG_E_HIP on this thread ("" if none). */
+const char *qgemv_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *qgemv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,276 @@
+"""Python binding of libqgemv.so (include/qgemv.h): batch-1 dequant-GEMV over
+GGUF block-quantized weights (Q8_0, Q4_0, MXFP4) on MI355X.
+
+The functions carry the C names and do argument marshalling only: torch
+tensors are turned into raw pointers and sizes, the caller's torch stream into
+a ``hipStream_t``, and a negative status into :class:`QgemvError`.  Every step
+of the computation runs in the library's HIP kernels; there is no other path.
+If ``libqgemv.so`` is missing, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Sequence
+
+Q8_0, Q4_0, MXFP4 = 1, 2, 3
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "mxfp4": MXFP4}
+MAX_WINDOWS = 64
+MAX_K = 65536
+
+QG_OK = 0
+STATUS = {
+    -1: "QG_E_NULL", -2: "QG_E_FMT", -3: "QG_E_SHAPE", -4: "QG_E_RANGE", -5: "QG_E_SIZE",
+    -6: "QG_E_ARG", -7: "QG_E_NOT_PINNED", -8: "QG_E_CAPACITY", -100: "QG_E_HIP",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+_i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = f"{where}: {self.name} ({status})"
+        if detail:
+            msg += f": {detail}"
+        super().__init__(msg)
+
+
+class qg_matrix(ctypes.Structure):
+    _fields_ = [("data", _vp), ("fmt", _i32), ("reserved", _i32), ("n_rows", _i64), ("k", _i64),
+                ("n_bytes", _i64)]
+
+
+class qg_window(ctypes.Structure):
+    _fields_ = [("data", _vp), ("n_rows", _i64), ("row_start", _i64), ("row_end", _i64),
+                ("x", _vp), ("y", _vp)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build() or "
+                           "python quantized_gemv_gguf_amd/build.py); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    sigs = {
+        "qgemv_block_bytes": ([_i32], _i64),
+        "qgemv_weight_bytes": ([_i32, _i64, _i64], _i64),
+        "qgemv_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
+        "qgemv_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
+        "qgemv_expert_windows": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _i64, _vp, _i64, _vp],
+                                 ctypes.c_int),
+        "qgemv_silu_mul": ([_vp, _vp, _vp, _i64, _vp], ctypes.c_int),
+        "qgemv_rms_carry": ([_vp, _vp, _i64, ctypes.c_float, _i32, _vp], ctypes.c_int),
+        "qgemv_dequant_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp], ctypes.c_int),
+        "qgemv_stream_create": ([_i64, _i32, P(_vp)], ctypes.c_int),
+        "qgemv_stream_ring_bytes": ([_vp], _i64),
+        "qgemv_stream_rows": ([_vp, P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+        "qgemv_stream_windows": ([_vp, _i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
+        "qgemv_stream_destroy": ([_vp], ctypes.c_int),
+        "qgemv_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "qgemv_last_hip_error": ([], ctypes.c_char_p),
+        "qgemv_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != QG_OK:
+        detail = lib().qgemv_strerror(rc).decode()
+        if rc == -100:
+            detail += ": " + lib().qgemv_last_hip_error().decode()
+        raise QgemvError(rc, where, detail)
+
+
+# --- marshalling helpers ------------------------------------------------------
+
+def _ptr(t) -> int:
+    """Raw address of a tensor (contiguity required), or 0 for None."""
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _f32(t, n: int, name: str):
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} values, needs {n}")
+    return _ptr(t)
+
+
+@dataclass
+class Matrix:
+    """A quantized matrix: ``data`` is a uint8 tensor of the raw blocks (device
+    memory for the resident calls, pinned host memory for the streamed ones)."""
+    data: object
+    fmt: int
+    n_rows: int
+    k: int
+
+    def c(self) -> qg_matrix:
+        return qg_matrix(_ptr(self.data), int(self.fmt), 0, int(self.n_rows), int(self.k),
+                         int(self.data.numel() * self.data.element_size()))
+
+
+@dataclass
+class Window:
+    """Rows [row_start, row_end) of ``mat`` with input ``x`` (k floats) and
+    output ``y`` (row_end - row_start floats)."""
+    mat: Matrix
+    row_start: int
+    row_end: int
+    x: object
+    y: object
+
+    def c(self) -> qg_window:
+        n = self.row_end - self.row_start
+        return qg_window(_ptr(self.mat.data), int(self.mat.n_rows), int(self.row_start), int(self.row_end),
+                         _f32(self.x, self.mat.k, "x"), _f32(self.y, max(n, 0), "y"))
+
+
+def _windows(ws: Sequence[Window]):
+    if len(ws) == 0:
+        return None, 0, None, None
+    fmt, k = ws[0].mat.fmt, ws[0].mat.k
+    arr = (qg_window * len(ws))(*[w.c() for w in ws])
+    return arr, len(ws), fmt, k
+
+
+# --- entry points ----------------------------------------------------------------
+
+def qgemv_block_bytes(fmt: int) -> int:
+    return int(lib().qgemv_block_bytes(fmt))
+
+
+def qgemv_weight_bytes(fmt: int, n_rows: int, k: int) -> int:
+    return int(lib().qgemv_weight_bytes(fmt, n_rows, k))
+
+
+def qgemv_rows(w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 0, stream=None) -> None:
+    m = w.c()
+    n = max(row_end - row_start, 0)
+    _check(lib().qgemv_rows(ctypes.byref(m), row_start, row_end, _f32(x, w.k, "x"), _f32(y, n, "y"),
+                            block_rows, _stream(stream)), "qgemv_rows")
+
+
+def qgemv_windows(windows: Sequence[Window], block_rows: int = 0, stream=None, fmt=None, k=None) -> None:
+    arr, n, f, kk = _windows(windows)
+    f = fmt if f is None else f
+    kk = k if kk is None else kk
+    _check(lib().qgemv_windows(int(f or Q8_0), int(kk or 32), arr, n, block_rows, _stream(stream)),
+           "qgemv_windows")
+
+
+def qgemv_expert_windows(mats: Sequence[Matrix], n_expert: int, ids, x, x_stride: int, y,
+                         block_rows: int = 0, stream=None) -> None:
+    ids = [int(i) for i in ids]
+    marr = (qg_matrix * len(mats))(*[m.c() for m in mats])
+    iarr = (_i32 * max(len(ids), 1))(*ids)
+    k = mats[0].k if mats else 32
+    out = (mats[0].n_rows // n_expert) if (mats and n_expert > 0) else 0
+    xp = _f32(x, k + (len(ids) - 1) * x_stride if ids else 0, "x")
+    yp = _f32(y, len(mats) * len(ids) * out, "y")
+    _check(lib().qgemv_expert_windows(marr, len(mats), n_expert, iarr, len(ids), xp, x_stride, yp,
+                                      block_rows, _stream(stream)), "qgemv_expert_windows")
+
+
+def qgemv_silu_mul(g, u, h, stream=None) -> None:
+    n = h.numel()
+    _check(lib().qgemv_silu_mul(_f32(g, n, "g"), _f32(u, n, "u"), _f32(h, n, "h"), n, _stream(stream)),
+           "qgemv_silu_mul")
+
+
+def qgemv_rms_carry(v, out, eps: float = 1e-6, gelu: bool = False, stream=None) -> None:
+    n = v.numel()
+    _check(lib().qgemv_rms_carry(_f32(v, n, "v"), _f32(out, n, "out"), n, float(eps), int(bool(gelu)),
+                                 _stream(stream)), "qgemv_rms_carry")
+
+
+def qgemv_dequant_rows(w: Matrix, row_start: int, row_end: int, out, stream=None) -> None:
+    m = w.c()
+    n = max(row_end - row_start, 0) * w.k
+    _check(lib().qgemv_dequant_rows(ctypes.byref(m), row_start, row_end, _f32(out, n, "out"),
+                                    _stream(stream)), "qgemv_dequant_rows")
+
+
+class Streamer:
+    """Owner of a qg_streamer: lookahead + 1 device slots of slot_bytes each."""
+
+    def __init__(self, slot_bytes: int, lookahead: int):
+        h = _vp()
+        _check(lib().qgemv_stream_create(int(slot_bytes), int(lookahead), ctypes.byref(h)),
+               "qgemv_stream_create")
+        self._h = h
+        self.slot_bytes = int(slot_bytes)
+        self.lookahead = int(lookahead)
+
+    @property
+    def ring_bytes(self) -> int:
+        return int(lib().qgemv_stream_ring_bytes(self._h))
+
+    def rows(self, w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 0, stream=None) -> None:
+        m = w.c()
+        n = max(row_end - row_start, 0)
+        _check(lib().qgemv_stream_rows(self._h, ctypes.byref(m), row_start, row_end, block_rows,
+                                       _f32(x, w.k, "x"), _f32(y, n, "y"), _stream(stream)),
+               "qgemv_stream_rows")
+
+    def windows(self, windows: Sequence[Window], block_rows: int = 0, stream=None) -> None:
+        arr, n, f, k = _windows(windows)
+        _check(lib().qgemv_stream_windows(self._h, int(f or Q8_0), int(k or 32), arr, n, block_rows,
+                                          _stream(stream)), "qgemv_stream_windows")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            h, self._h = self._h, None
+            _check(lib().qgemv_stream_destroy(h), "qgemv_stream_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def qgemv_stream_create(slot_bytes: int, lookahead: int) -> Streamer:
+    return Streamer(slot_bytes, lookahead)
+
+
+def qgemv_version() -> str:
+    return lib().qgemv_version().decode()

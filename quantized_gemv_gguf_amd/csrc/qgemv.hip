@@ -1,0 +1,783 @@
+// qgemv.hip -- gfx950 kernels and the C ABI of libqgemv.so (see include/qgemv.h).
+//
+// Batch-1 dequant-GEMV over GGUF blocks (Q8_0, Q4_0, MXFP4): every output row
+// is a dot product of its dequantized weights with an fp32 activation vector,
+// accumulated in fp32, the weights decoded in registers and never written out
+// (neurostream README, "How it works", step 5: the fused decode-path GEMV).
+// Single-batch decode reads every active weight once per token, so the
+// kernels are bound by weight bytes moved (neurostream README, "The idea":
+// tokens/sec = effective bandwidth / active bytes per token).  No MFMA: a
+// matrix-vector product has no operand reuse to feed a matrix core.
+//
+// Work decomposition
+//   A "team" is one workgroup of WT wavefronts (T = 64 * WT lanes).  Team lane
+//   t owns the block columns j = t + T*c (c < C) of every row it touches, and
+//   keeps the 32 activations of each such column in registers, loaded once per
+//   window.  A row is one pass: each lane dots its C blocks (32 weights each),
+//   the 64 lanes of a wave are combined by a fixed xor butterfly, and for
+//   WT > 1 the per-wave sums go through LDS and are added in wave order.
+//   (WT, C) is a function of (format, k) only, and so is the whole per-row
+//   operation order: a row gives the same bits whichever window, row block,
+//   tile, team, launch or stream computes it, resident or streamed.
+//
+//   Rows are cut into tiles that never straddle a row block (block_rows), the
+//   tiles of all windows are numbered in window order, and team b takes the
+//   contiguous tile range [b*tpt, (b+1)*tpt), so a team meets few windows and
+//   reloads its activations only when the window changes.
+//
+// Matrix layout: row-major [n_rows][k/32 blocks], y[o] = sum_i W[o, i] x[i]
+// (RAMforge README, "Milestone 6", matrix layout).  Each row is a whole number
+// of blocks, so a row window is one contiguous byte range (neurostream README,
+// "The idea").
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "qgemv.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxWindows = QG_MAX_WINDOWS;
+constexpr int kMaxC = 4;         // block columns per lane
+constexpr int kMaxWT = 8;        // waves per team
+constexpr int kTileRowsMulti = 8;  // rows per tile when a team spans several waves
+
+// ---------------------------------------------------------------------------
+// Formats: block bytes and the in-register block decoders.  A decoder turns
+// one block into 32 "unit" values u_j and a block scale such that the weight
+// is w_j = scale(u_j); the GEMV applies the scale once to the block's partial
+// dot product, the dequant kernel applies it to every u_j.  Both go through
+// the same code, so the bit-exact decode check covers the GEMV's decoder.
+// ---------------------------------------------------------------------------
+
+template <int FMT> struct Fmt;
+
+// Q8_0: fp16 d, 32 x int8 q; w = d * q (RAMforge README, "Milestone 5").
+template <> struct Fmt<QG_Q8_0> {
+  static constexpr int kBytes = 34;
+  struct Scale { float d; };
+  __device__ static inline Scale load(const uint8_t *p, float u[32]) {
+    uint16_t db;
+    u32x4 a, b;
+    __builtin_memcpy(&db, p, 2);
+    __builtin_memcpy(&a, p + 2, 16);
+    __builtin_memcpy(&b, p + 18, 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u[4 * i + k] = (float)(int8_t)(a[i] >> (8 * k));
+        u[16 + 4 * i + k] = (float)(int8_t)(b[i] >> (8 * k));
+      }
+    }
+    return Scale{__half2float(__ushort_as_half(db))};
+  }
+  __device__ static inline float apply(Scale s, float v) { return s.d * v; }
+  __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d, v, acc); }
+};
+
+// Q4_0: fp16 d, 16 bytes of nibbles; w = d * (q - 8) (RAMforge README,
+// "Milestone 5").  Element j < 16 is the low nibble of byte j, element j + 16
+// the high nibble.  (q ^ 8) is q - 8 in 4-bit two's complement; moved to the
+// top of a byte it reads as the int8 16 * (q - 8), exactly, and the 1/16 goes
+// into the scale (a power of two, so d/16 is exact too).
+template <> struct Fmt<QG_Q4_0> {
+  static constexpr int kBytes = 18;
+  struct Scale { float d16; };
+  __device__ static inline Scale load(const uint8_t *p, float u[32]) {
+    uint16_t db;
+    u32x4 q;
+    __builtin_memcpy(&db, p, 2);
+    __builtin_memcpy(&q, p + 2, 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = q[i] ^ 0x88888888u;
+      const uint32_t hi = v & 0xF0F0F0F0u;
+      const uint32_t lo = (v << 4) & 0xF0F0F0F0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u[4 * i + k] = (float)(int8_t)(lo >> (8 * k));
+        u[16 + 4 * i + k] = (float)(int8_t)(hi >> (8 * k));
+      }
+    }
+    return Scale{__half2float(__ushort_as_half(db)) * 0.0625f};
+  }
+  __device__ static inline float apply(Scale s, float v) { return s.d16 * v; }
+  __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d16, v, acc); }
+};
+
+// MXFP4: E8M0 e, 16 bytes of E2M1 nibbles; w = 2^(e-127) * E2M1(nib) (block
+// size from neurostream README, "The idea": 4.41 MB per 2,880 x 2,880 expert).
+// gfx950's v_cvt_scalef32_pk_f32_fp4 turns both nibbles of a byte into fp32
+// (scale 1.0: the E2M1 value itself, exact); the E8M0 scale is applied with an
+// exact ldexp, and e = 255 gives NaN.
+template <> struct Fmt<QG_MXFP4> {
+  static constexpr int kBytes = 17;
+  struct Scale { int e; };
+  // f = (value of the byte's low nibble, value of its high nibble)
+  template <typename V2>
+  __device__ static inline void unpack(uint32_t, V2 f, float *u) {
+    u[0] = f[0];
+    u[16] = f[1];
+  }
+  __device__ static inline Scale load(const uint8_t *p, float u[32]) {
+    u32x4 q;
+    const int e = p[0];
+    __builtin_memcpy(&q, p + 1, 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 0), u + 4 * i + 0);
+      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 1), u + 4 * i + 1);
+      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 2), u + 4 * i + 2);
+      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 3), u + 4 * i + 3);
+    }
+    return Scale{e};
+  }
+  __device__ static inline float apply(Scale s, float v) {
+    return s.e == 255 ? __builtin_nanf("") : ldexpf(v, s.e - 127);
+  }
+  __device__ static inline float fma_acc(Scale s, float v, float acc) { return acc + apply(s, v); }
+};
+
+// ---------------------------------------------------------------------------
+// GEMV kernel
+// ---------------------------------------------------------------------------
+
+struct WinDev {
+  const uint8_t *base;  // row 0 of the window's matrix
+  const float *x;
+  float *y;             // y[r - row_start] <-> row r
+  int64_t row_start, row_end;
+};
+
+struct GemvArgs {
+  WinDev win[kMaxWindows];
+  int32_t tile_prefix[kMaxWindows + 1];  // tiles of windows [0, w)
+  int64_t row_bytes;
+  int64_t block_rows;  // > 0 (the host replaces 0 by a bound above every window)
+  int32_t n_win, nb, tile_rows, tiles_per_team, n_tiles;
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // Fixed xor butterfly: every lane ends with the same, order-fixed sum.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int FMT, int WT, int C>
+__global__ void __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(2)))
+gemv_kernel(const GemvArgs a) {
+  using F = Fmt<FMT>;
+  constexpr int T = 64 * WT;
+  const int tl = threadIdx.x;
+  const int lane = tl & 63;
+  const int wave = tl >> 6;
+
+  __shared__ float red[2][WT][kTileRowsMulti];
+
+  const int t_begin = blockIdx.x * a.tiles_per_team;
+  const int t_end = min(t_begin + a.tiles_per_team, a.n_tiles);
+  const int nb = a.nb;
+  const int64_t rbytes = a.row_bytes;
+
+  float xr[C][32];
+  int cur = -1;
+  int w = 0;
+  int parity = 0;
+
+  for (int t = t_begin; t < t_end; ++t) {
+    while (t >= a.tile_prefix[w + 1]) ++w;
+    const WinDev W = a.win[w];
+    if (w != cur) {
+      cur = w;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = tl + T * c;
+        if (j < nb) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            float4 v;
+            __builtin_memcpy(&v, W.x + 32 * j + 4 * q, 16);
+            xr[c][4 * q + 0] = v.x;
+            xr[c][4 * q + 1] = v.y;
+            xr[c][4 * q + 2] = v.z;
+            xr[c][4 * q + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 32; ++e) xr[c][e] = 0.0f;
+        }
+      }
+    }
+    // tile -> rows [r0, r1), never across a row block
+    const int64_t tt = t - a.tile_prefix[w];
+    const int64_t B = a.block_rows;
+    const int64_t tpb = (B + a.tile_rows - 1) / a.tile_rows;
+    const int64_t blk = tt / tpb, tib = tt - blk * tpb;
+    const int64_t r0 = W.row_start + blk * B + tib * a.tile_rows;
+    int64_t r1 = r0 + a.tile_rows;
+    r1 = min(r1, W.row_start + (blk + 1) * B);
+    r1 = min(r1, W.row_end);
+
+    for (int64_t r = r0; r < r1; r += 2) {
+      const bool two = (r + 1 < r1);
+      const uint8_t *row0 = W.base + r * rbytes;
+      const uint8_t *row1 = two ? row0 + rbytes : row0;
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = tl + T * c;
+        if (j < nb) {
+          float u0[32], u1[32];
+          const auto s0 = F::load(row0 + (int64_t)F::kBytes * j, u0);
+          const auto s1 = F::load(row1 + (int64_t)F::kBytes * j, u1);
+          float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            p0[e & 3] = fmaf(u0[e], xr[c][e], p0[e & 3]);
+            p1[e & 3] = fmaf(u1[e], xr[c][e], p1[e & 3]);
+          }
+          acc0 = F::fma_acc(s0, (p0[0] + p0[1]) + (p0[2] + p0[3]), acc0);
+          acc1 = F::fma_acc(s1, (p1[0] + p1[1]) + (p1[2] + p1[3]), acc1);
+        }
+      }
+      acc0 = wave_sum(acc0);
+      acc1 = wave_sum(acc1);
+      if (WT == 1) {
+        if (lane == 0) W.y[r - W.row_start] = acc0;
+        if (lane == 1 && two) W.y[r + 1 - W.row_start] = acc1;
+      } else {
+        const int i = (int)(r - r0);
+        if (lane == 0) red[parity][wave][i] = acc0;
+        if (lane == 1 && two) red[parity][wave][i + 1] = acc1;
+      }
+    }
+    if (WT > 1) {
+      __syncthreads();
+      const int n = (int)(r1 - r0);
+      if (tl < n) {
+        float s = red[parity][0][tl];
+#pragma unroll
+        for (int v = 1; v < WT; ++v) s += red[parity][v][tl];
+        W.y[r0 + tl - W.row_start] = s;
+      }
+      parity ^= 1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequant (test aid), SiLU*up, RMS carry
+// ---------------------------------------------------------------------------
+
+template <int FMT>
+__global__ void dequant_kernel(const uint8_t *base, int64_t row_start, int64_t n_rows, int nb,
+                               int64_t row_bytes, float *out) {
+  using F = Fmt<FMT>;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= n_rows * nb) return;
+  const int64_t r = id / nb;
+  const int j = (int)(id - r * nb);
+  float u[32];
+  const auto s = F::load(base + (row_start + r) * row_bytes + (int64_t)F::kBytes * j, u);
+  float *o = out + r * (int64_t)nb * 32 + 32 * j;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) o[e] = F::apply(s, u[e]);
+}
+
+__global__ void silu_mul_kernel(const float *g, const float *u, float *h, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float v = g[i];
+    h[i] = v / (1.0f + expf(-v)) * u[i];
+  }
+}
+
+constexpr int kCarryThreads = 1024;
+
+__global__ void __launch_bounds__(kCarryThreads)
+rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
+  __shared__ float part[kCarryThreads / 64];
+  const int tid = threadIdx.x;
+  float ss = 0.0f;
+  for (int64_t i = tid; i < n; i += kCarryThreads) {
+    float t = v[i];
+    if (gelu) t = 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
+    ss = fmaf(t, t, ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kCarryThreads / 64; ++i) tot += part[i];
+  const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+  for (int64_t i = tid; i < n; i += kCarryThreads) {
+    float t = v[i];
+    if (gelu) t = 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
+    out[i] = t * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+thread_local std::string g_last_hip;
+
+int hip_fail(hipError_t e, const char *what) {
+  g_last_hip = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return QG_E_HIP;
+}
+
+#define QG_HIP(call)                                    \
+  do {                                                  \
+    hipError_t e_ = (call);                             \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);   \
+  } while (0)
+
+int block_bytes(int32_t fmt) {
+  switch (fmt) {
+    case QG_Q8_0: return Fmt<QG_Q8_0>::kBytes;
+    case QG_Q4_0: return Fmt<QG_Q4_0>::kBytes;
+    case QG_MXFP4: return Fmt<QG_MXFP4>::kBytes;
+    default: return QG_E_FMT;
+  }
+}
+
+int check_fmt_k(int32_t fmt, int64_t k) {
+  if (block_bytes(fmt) < 0) return QG_E_FMT;
+  if (k <= 0 || k % 32 != 0) return QG_E_SHAPE;
+  return QG_OK;
+}
+
+// Team shape (WT waves, C block columns per lane) -- a function of k only.
+struct Shape { int wt, c; };
+int team_shape(int64_t k, Shape *s) {
+  const int64_t nb = k / 32;
+  for (int wt = 1; wt <= kMaxWT; wt *= 2) {
+    const int64_t c = (nb + 64 * wt - 1) / (64 * wt);
+    if (c <= kMaxC) { s->wt = wt; s->c = (int)c; return QG_OK; }
+  }
+  return QG_E_SHAPE;  // k above 64 * kMaxWT * kMaxC * 32 = 65536
+}
+
+int check_matrix(const qg_matrix *w) {
+  if (!w) return QG_E_NULL;
+  int rc = check_fmt_k(w->fmt, w->k);
+  if (rc) return rc;
+  if (w->n_rows < 0 || w->reserved != 0) return w->n_rows < 0 ? QG_E_SHAPE : QG_E_ARG;
+  Shape s;
+  if ((rc = team_shape(w->k, &s))) return rc;
+  if (w->n_bytes != w->n_rows * (w->k / 32) * block_bytes(w->fmt)) return QG_E_SIZE;
+  if (!w->data && w->n_bytes > 0) return QG_E_NULL;
+  return QG_OK;
+}
+
+int check_range(int64_t n_rows, int64_t r0, int64_t r1) {
+  if (r0 < 0 || r0 > r1 || r1 > n_rows) return QG_E_RANGE;
+  return QG_OK;
+}
+
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+typedef void (*GemvFn)(GemvArgs);
+
+template <int FMT, int WT>
+GemvFn pick_c(int c) {
+  switch (c) {
+    case 1: return gemv_kernel<FMT, WT, 1>;
+    case 2: return gemv_kernel<FMT, WT, 2>;
+    case 3: return gemv_kernel<FMT, WT, 3>;
+    default: return gemv_kernel<FMT, WT, 4>;
+  }
+}
+
+template <int FMT>
+GemvFn pick_wt(int wt, int c) {
+  switch (wt) {
+    case 1: return pick_c<FMT, 1>(c);
+    case 2: return pick_c<FMT, 2>(c);
+    case 4: return pick_c<FMT, 4>(c);
+    default: return pick_c<FMT, 8>(c);
+  }
+}
+
+GemvFn pick(int32_t fmt, Shape s) {
+  switch (fmt) {
+    case QG_Q8_0: return pick_wt<QG_Q8_0>(s.wt, s.c);
+    case QG_Q4_0: return pick_wt<QG_Q4_0>(s.wt, s.c);
+    default: return pick_wt<QG_MXFP4>(s.wt, s.c);
+  }
+}
+
+// Launch one grid over n windows (already validated).  win[i].data is the
+// device address of the window's matrix row 0.
+int launch_gemv(int32_t fmt, int64_t k, const qg_window *win, int n, int64_t block_rows,
+                hipStream_t stream) {
+  Shape s;
+  int rc = team_shape(k, &s);
+  if (rc) return rc;
+  GemvArgs a;
+  memset(&a, 0, sizeof(a));
+  const int tile_rows = s.wt == 1 ? 2 : kTileRowsMulti;
+  int64_t maxlen = 1;
+  for (int i = 0; i < n; ++i) maxlen = std::max<int64_t>(maxlen, win[i].row_end - win[i].row_start);
+  const int64_t B = block_rows > 0 ? block_rows : maxlen;
+  int64_t tiles = 0;
+  int m = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t len = win[i].row_end - win[i].row_start;
+    if (len == 0) continue;
+    const int64_t tpb = (B + tile_rows - 1) / tile_rows;
+    const int64_t full = len / B, rem = len - full * B;
+    a.win[m].base = (const uint8_t *)win[i].data;
+    a.win[m].x = win[i].x;
+    a.win[m].y = win[i].y;
+    a.win[m].row_start = win[i].row_start;
+    a.win[m].row_end = win[i].row_end;
+    a.tile_prefix[m] = (int32_t)tiles;
+    tiles += full * tpb + (rem + tile_rows - 1) / tile_rows;
+    ++m;
+  }
+  if (m == 0) return QG_OK;
+  if (tiles > INT32_MAX / 2) return QG_E_SHAPE;
+  a.tile_prefix[m] = (int32_t)tiles;
+  for (int i = m + 1; i <= kMaxWindows; ++i) a.tile_prefix[i] = (int32_t)tiles;
+  a.n_win = m;
+  a.nb = (int32_t)(k / 32);
+  a.row_bytes = (k / 32) * block_bytes(fmt);
+  a.block_rows = B;
+  a.tile_rows = tile_rows;
+  a.n_tiles = (int32_t)tiles;
+  const int64_t teams_max = (int64_t)device_cus() * 8 / s.wt;
+  int64_t teams = std::min<int64_t>(teams_max, tiles);
+  const int64_t tpt = (tiles + teams - 1) / teams;
+  teams = (tiles + tpt - 1) / tpt;
+  a.tiles_per_team = (int32_t)tpt;
+  hipLaunchKernelGGL(pick(fmt, s), dim3((unsigned)teams), dim3(64 * s.wt), 0, stream, a);
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+int validate_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win, int64_t block_rows) {
+  int rc = check_fmt_k(fmt, k);
+  if (rc) return rc;
+  Shape s;
+  if ((rc = team_shape(k, &s))) return rc;
+  if (n_win < 0 || n_win > kMaxWindows || block_rows < 0) return QG_E_ARG;
+  if (n_win > 0 && !win) return QG_E_NULL;
+  for (int i = 0; i < n_win; ++i) {
+    if (win[i].n_rows < 0) return QG_E_SHAPE;
+    if ((rc = check_range(win[i].n_rows, win[i].row_start, win[i].row_end))) return rc;
+    if (win[i].row_end > win[i].row_start && (!win[i].data || !win[i].x || !win[i].y)) return QG_E_NULL;
+  }
+  return QG_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+struct qg_streamer {
+  int device;
+  int64_t slot_bytes;
+  int lookahead;
+  uint8_t *ring;
+  hipStream_t copy;
+  std::vector<hipEvent_t> ready, freed;
+  std::vector<char> freed_valid;
+  uint64_t next;
+};
+
+extern "C" {
+
+const char *qgemv_version(void) { return "0.1.0"; }
+
+const char *qgemv_strerror(int status) {
+  switch (status) {
+    case QG_OK: return "ok";
+    case QG_E_NULL: return "a required pointer is NULL";
+    case QG_E_FMT: return "unknown quantization format";
+    case QG_E_SHAPE: return "bad shape (k must be a positive multiple of 32, at most 65536; n_rows >= 0)";
+    case QG_E_RANGE: return "row range or expert id out of range";
+    case QG_E_SIZE: return "n_bytes does not match n_rows * (k/32) * block bytes";
+    case QG_E_ARG: return "bad argument (block_rows, lookahead, window count, n, eps or stride)";
+    case QG_E_NOT_PINNED: return "streamed weights are not in page-locked host memory";
+    case QG_E_CAPACITY: return "a row block is larger than a ring slot";
+    case QG_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *qgemv_last_hip_error(void) { return g_last_hip.c_str(); }
+
+int64_t qgemv_block_bytes(int32_t fmt) { return block_bytes(fmt); }
+
+int64_t qgemv_weight_bytes(int32_t fmt, int64_t n_rows, int64_t k) {
+  int rc = check_fmt_k(fmt, k);
+  if (rc) return rc;
+  if (n_rows < 0) return QG_E_SHAPE;
+  return n_rows * (k / 32) * block_bytes(fmt);
+}
+
+int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, float *y,
+               int64_t block_rows, qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  if (block_rows < 0) return QG_E_ARG;
+  if (row_end == row_start) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  qg_window win = {w->data, w->n_rows, row_start, row_end, x, y};
+  return launch_gemv(w->fmt, w->k, &win, 1, block_rows, stream);
+}
+
+int qgemv_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win, int64_t block_rows,
+                  qg_stream_t stream) {
+  int rc = validate_windows(fmt, k, win, n_win, block_rows);
+  if (rc) return rc;
+  if (n_win == 0) return QG_OK;
+  return launch_gemv(fmt, k, win, n_win, block_rows, stream);
+}
+
+int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert, const int32_t *ids,
+                         int32_t n_sel, const float *x, int64_t x_stride, float *y, int64_t block_rows,
+                         qg_stream_t stream) {
+  if (!mats || (n_sel > 0 && !ids)) return QG_E_NULL;
+  if (n_mat < 1 || n_sel < 0 || (int64_t)n_mat * n_sel > kMaxWindows || x_stride < 0 || block_rows < 0)
+    return QG_E_ARG;
+  if (n_expert <= 0) return QG_E_SHAPE;
+  int rc;
+  for (int m = 0; m < n_mat; ++m) {
+    if ((rc = check_matrix(&mats[m]))) return rc;
+    if (mats[m].fmt != mats[0].fmt || mats[m].k != mats[0].k || mats[m].n_rows != mats[0].n_rows)
+      return QG_E_SHAPE;
+  }
+  if (mats[0].n_rows % n_expert != 0) return QG_E_SHAPE;
+  const int64_t out = mats[0].n_rows / n_expert;
+  for (int s = 0; s < n_sel; ++s)
+    if (ids[s] < 0 || ids[s] >= n_expert) return QG_E_RANGE;
+  if (n_sel == 0 || out == 0) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  qg_window win[kMaxWindows];
+  int n = 0;
+  for (int m = 0; m < n_mat; ++m)
+    for (int s = 0; s < n_sel; ++s) {
+      win[n].data = mats[m].data;
+      win[n].n_rows = mats[m].n_rows;
+      win[n].row_start = (int64_t)ids[s] * out;
+      win[n].row_end = (int64_t)(ids[s] + 1) * out;
+      win[n].x = x + (int64_t)s * x_stride;
+      win[n].y = y + ((int64_t)m * n_sel + s) * out;
+      ++n;
+    }
+  return launch_gemv(mats[0].fmt, mats[0].k, win, n, block_rows, stream);
+}
+
+int qgemv_silu_mul(const float *g, const float *u, float *h, int64_t n, qg_stream_t stream) {
+  if (n < 0) return QG_E_ARG;
+  if (n == 0) return QG_OK;
+  if (!g || !u || !h) return QG_E_NULL;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, u, h, n);
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+int qgemv_rms_carry(const float *v, float *out, int64_t n, float eps, int32_t gelu, qg_stream_t stream) {
+  if (n < 1 || !(eps >= 0.0f) || (gelu != 0 && gelu != 1)) return QG_E_ARG;
+  if (!v || !out) return QG_E_NULL;
+  hipLaunchKernelGGL(rms_carry_kernel, dim3(1), dim3(kCarryThreads), 0, stream, v, out, n, eps, (int)gelu);
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, float *out,
+                       qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  if (row_end == row_start) return QG_OK;
+  if (!out) return QG_E_NULL;
+  const int nb = (int)(w->k / 32);
+  const int64_t rb = (w->k / 32) * block_bytes(w->fmt);
+  const int64_t n = (row_end - row_start) * nb;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  const uint8_t *base = (const uint8_t *)w->data;
+  switch (w->fmt) {
+    case QG_Q8_0:
+      hipLaunchKernelGGL(dequant_kernel<QG_Q8_0>, dim3(blocks), dim3(256), 0, stream, base, row_start,
+                         row_end - row_start, nb, rb, out);
+      break;
+    case QG_Q4_0:
+      hipLaunchKernelGGL(dequant_kernel<QG_Q4_0>, dim3(blocks), dim3(256), 0, stream, base, row_start,
+                         row_end - row_start, nb, rb, out);
+      break;
+    default:
+      hipLaunchKernelGGL(dequant_kernel<QG_MXFP4>, dim3(blocks), dim3(256), 0, stream, base, row_start,
+                         row_end - row_start, nb, rb, out);
+  }
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+// ---- streamer ---------------------------------------------------------------
+
+int qgemv_stream_create(int64_t slot_bytes, int32_t lookahead, qg_streamer **out) {
+  if (!out) return QG_E_NULL;
+  if (slot_bytes < 1 || lookahead < 1 || lookahead > 64) return QG_E_ARG;
+  *out = nullptr;
+  qg_streamer *st = new qg_streamer();
+  st->slot_bytes = slot_bytes;
+  st->lookahead = lookahead;
+  st->ring = nullptr;
+  st->copy = nullptr;
+  st->next = 0;
+  const int n = lookahead + 1;
+  auto fail = [&](hipError_t e, const char *what) {
+    int rc = hip_fail(e, what);
+    qgemv_stream_destroy(st);
+    return rc;
+  };
+  hipError_t e;
+  if ((e = hipGetDevice(&st->device)) != hipSuccess) return fail(e, "hipGetDevice");
+  if ((e = hipMalloc((void **)&st->ring, (size_t)slot_bytes * n)) != hipSuccess) return fail(e, "hipMalloc(ring)");
+  if ((e = hipStreamCreateWithFlags(&st->copy, hipStreamNonBlocking)) != hipSuccess)
+    return fail(e, "hipStreamCreateWithFlags");
+  st->ready.assign(n, nullptr);
+  st->freed.assign(n, nullptr);
+  st->freed_valid.assign(n, 0);
+  for (int i = 0; i < n; ++i) {
+    if ((e = hipEventCreateWithFlags(&st->ready[i], hipEventDisableTiming)) != hipSuccess)
+      return fail(e, "hipEventCreateWithFlags");
+    if ((e = hipEventCreateWithFlags(&st->freed[i], hipEventDisableTiming)) != hipSuccess)
+      return fail(e, "hipEventCreateWithFlags");
+  }
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e, "hipDeviceSynchronize");
+  *out = st;
+  return QG_OK;
+}
+
+int64_t qgemv_stream_ring_bytes(const qg_streamer *st) {
+  if (!st) return QG_E_NULL;
+  return st->slot_bytes * (st->lookahead + 1);
+}
+
+int qgemv_stream_destroy(qg_streamer *st) {
+  if (!st) return QG_OK;
+  int rc = QG_OK;
+  hipError_t e;
+  if (st->copy && (e = hipStreamSynchronize(st->copy)) != hipSuccess) rc = hip_fail(e, "hipStreamSynchronize");
+  for (auto ev : st->freed)
+    if (ev) {
+      if ((e = hipEventSynchronize(ev)) != hipSuccess && rc == QG_OK) rc = hip_fail(e, "hipEventSynchronize");
+      (void)hipEventDestroy(ev);
+    }
+  for (auto ev : st->ready)
+    if (ev) (void)hipEventDestroy(ev);
+  if (st->copy) (void)hipStreamDestroy(st->copy);
+  if (st->ring) (void)hipFree(st->ring);
+  delete st;
+  return rc;
+}
+
+namespace {
+
+int check_pinned(const void *p) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return QG_E_NOT_PINNED;
+  }
+  if (attr.type != hipMemoryTypeHost) return QG_E_NOT_PINNED;
+  return QG_OK;
+}
+
+// Stream the row blocks of validated windows through the ring.
+int stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win, int n_win,
+                   int64_t block_rows, hipStream_t stream) {
+  const int64_t rb = (k / 32) * block_bytes(fmt);
+  const int nslot = st->lookahead + 1;
+  // every block must fit a slot; check all before enqueueing anything
+  for (int i = 0; i < n_win; ++i) {
+    const int64_t len = win[i].row_end - win[i].row_start;
+    if (len == 0) continue;
+    const int64_t B = block_rows > 0 ? std::min(block_rows, len) : len;
+    if (B * rb > st->slot_bytes) return QG_E_CAPACITY;
+    int rc = check_pinned(win[i].data);
+    if (rc) return rc;
+  }
+  for (int i = 0; i < n_win; ++i) {
+    const int64_t len = win[i].row_end - win[i].row_start;
+    const int64_t B = block_rows > 0 ? block_rows : len;
+    for (int64_t r = win[i].row_start; r < win[i].row_end; r += B) {
+      const int64_t n = std::min(B, win[i].row_end - r);
+      const int slot = (int)(st->next++ % (uint64_t)nslot);
+      uint8_t *dst = st->ring + (int64_t)slot * st->slot_bytes;
+      if (st->freed_valid[slot]) QG_HIP(hipStreamWaitEvent(st->copy, st->freed[slot], 0));
+      QG_HIP(hipMemcpyAsync(dst, (const uint8_t *)win[i].data + r * rb, (size_t)(n * rb),
+                            hipMemcpyHostToDevice, st->copy));
+      QG_HIP(hipEventRecord(st->ready[slot], st->copy));
+      QG_HIP(hipStreamWaitEvent(stream, st->ready[slot], 0));
+      qg_window blk = {dst, n, 0, n, win[i].x, win[i].y + (r - win[i].row_start)};
+      int rc = launch_gemv(fmt, k, &blk, 1, 0, stream);
+      if (rc) return rc;
+      QG_HIP(hipEventRecord(st->freed[slot], stream));
+      st->freed_valid[slot] = 1;
+    }
+  }
+  return QG_OK;
+}
+
+}  // namespace
+
+int qgemv_stream_rows(qg_streamer *st, const qg_matrix *w, int64_t row_start, int64_t row_end,
+                      int64_t block_rows, const float *x, float *y, qg_stream_t stream) {
+  if (!st) return QG_E_NULL;
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  if (block_rows < 0) return QG_E_ARG;
+  if (row_end == row_start) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  qg_window win = {w->data, w->n_rows, row_start, row_end, x, y};
+  return stream_windows(st, w->fmt, w->k, &win, 1, block_rows, stream);
+}
+
+int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win, int32_t n_win,
+                         int64_t block_rows, qg_stream_t stream) {
+  if (!st) return QG_E_NULL;
+  int rc = validate_windows(fmt, k, win, n_win, block_rows);
+  if (rc) return rc;
+  if (n_win == 0) return QG_OK;
+  return stream_windows(st, fmt, k, win, n_win, block_rows, stream);
+}
+
+}  // extern "C"
