@@ -68,7 +68,8 @@ enum qg_status {
                            oversized tensors are rejected: RAMforge README,
                            "Build & Test", quant.rs unit tests) */
   QG_E_ARG = -6,        /* block_rows < 0, lookahead < 1, n_win < 0 or above
-                           QG_MAX_WINDOWS, n < 0, bad eps, x_stride < 0 */
+                           QG_MAX_WINDOWS, n < 0, bad eps, x_stride < 0,
+                           weight data not 16-byte aligned */
   QG_E_NOT_PINNED = -7, /* streamed weights not in page-locked host memory */
   QG_E_CAPACITY = -8,   /* a streamed row block is larger than a ring slot */
   QG_E_HIP = -100       /* a HIP runtime call failed; see qgemv_last_hip_error */
@@ -78,14 +79,17 @@ enum qg_status {
 #define QG_MAX_WINDOWS 64
 
 /* Largest k: a row's block columns are spread over at most 8 wavefronts with
- * at most 4 columns per lane, each lane holding its activations in registers. */
-#define QG_MAX_K 65536
+ * at most 3 columns per lane, each lane holding its activations in registers. */
+#define QG_MAX_K 49152
 
 /* A whole quantized weight matrix: the compact resident representation of a
  * quantized tensor (RAMforge README, "Milestone 5", QuantizedTensor: raw block
  * bytes plus type and shape). */
 typedef struct qg_matrix {
-  const void *data; /* n_bytes of blocks, row-major [n_rows][k/32] */
+  const void *data; /* n_bytes of blocks, row-major [n_rows][k/32]; 16-byte
+                       aligned.  Kernels fetch whole aligned 16-byte granules,
+                       so they may read up to 15 bytes past the last row
+                       inside the granule holding its last byte. */
   int32_t fmt;      /* enum qg_format */
   int32_t reserved; /* must be 0 */
   int64_t n_rows;   /* output rows */
@@ -97,7 +101,7 @@ typedef struct qg_matrix {
  * (neurostream README, "How it works", step 4: row_start/row_end bound the
  * walk over a weight matrix).  All windows of one call share fmt and k. */
 typedef struct qg_window {
-  const void *data;  /* the matrix's row 0 (not the window's first row) */
+  const void *data;  /* the matrix's row 0 (not the window's first row); 16-byte aligned */
   int64_t n_rows;    /* rows of that matrix, for range checks */
   int64_t row_start; /* first row of the window */
   int64_t row_end;   /* one past the last row */

@@ -17,7 +17,7 @@ from typing import Sequence
 Q8_0, Q4_0, MXFP4 = 1, 2, 3
 FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "mxfp4": MXFP4}
 MAX_WINDOWS = 64
-MAX_K = 65536
+MAX_K = 49152
 
 QG_OK = 0
 STATUS = {

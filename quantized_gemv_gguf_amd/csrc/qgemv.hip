@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "qgemv.h"
@@ -47,39 +48,33 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWindows = QG_MAX_WINDOWS;
-constexpr int kMaxC = 4;         // block columns per lane
-constexpr int kMaxWT = 8;        // waves per team
-constexpr int kTileRowsMulti = 8;  // rows per tile when a team spans several waves
+constexpr int kMaxC = 2;         // block columns per lane
+constexpr int kMaxWT = 12;       // waves per team
 
 // ---------------------------------------------------------------------------
-// Formats: block bytes and the in-register block decoders.  A decoder turns
-// one block into 32 "unit" values u_j and a block scale such that the weight
-// is w_j = scale(u_j); the GEMV applies the scale once to the block's partial
-// dot product, the dequant kernel applies it to every u_j.  Both go through
-// the same code, so the bit-exact decode check covers the GEMV's decoder.
+// Formats.  A block is a scale field followed by a payload of kWords 32-bit
+// words.  decode() turns the payload into 32 "unit" values u_j and scale()
+// the scale field into a Scale such that the weight is w_j = apply(scale, u_j);
+// the GEMV applies the scale once to a block's partial dot product, the
+// dequant kernel applies it to every u_j.  Both use the same decoder, so the
+// bit-exact decode check covers the GEMV's decoder.
 // ---------------------------------------------------------------------------
 
 template <int FMT> struct Fmt;
 
 // Q8_0: fp16 d, 32 x int8 q; w = d * q (RAMforge README, "Milestone 5").
 template <> struct Fmt<QG_Q8_0> {
-  static constexpr int kBytes = 34;
+  static constexpr int kBytes = 34, kScaleBytes = 2, kWords = 8;
   struct Scale { float d; };
-  __device__ static inline Scale load(const uint8_t *p, float u[32]) {
-    uint16_t db;
-    u32x4 a, b;
-    __builtin_memcpy(&db, p, 2);
-    __builtin_memcpy(&a, p + 2, 16);
-    __builtin_memcpy(&b, p + 18, 16);
+  __device__ static inline Scale scale(uint32_t bits) {
+    return Scale{__half2float(__ushort_as_half((uint16_t)bits))};
+  }
+  __device__ static inline void decode(const uint32_t *q, float u[32]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        u[4 * i + k] = (float)(int8_t)(a[i] >> (8 * k));
-        u[16 + 4 * i + k] = (float)(int8_t)(b[i] >> (8 * k));
-      }
+      for (int k = 0; k < 4; ++k) u[4 * i + k] = (float)(int8_t)(q[i] >> (8 * k));
     }
-    return Scale{__half2float(__ushort_as_half(db))};
   }
   __device__ static inline float apply(Scale s, float v) { return s.d * v; }
   __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d, v, acc); }
@@ -91,13 +86,12 @@ template <> struct Fmt<QG_Q8_0> {
 // top of a byte it reads as the int8 16 * (q - 8), exactly, and the 1/16 goes
 // into the scale (a power of two, so d/16 is exact too).
 template <> struct Fmt<QG_Q4_0> {
-  static constexpr int kBytes = 18;
+  static constexpr int kBytes = 18, kScaleBytes = 2, kWords = 4;
   struct Scale { float d16; };
-  __device__ static inline Scale load(const uint8_t *p, float u[32]) {
-    uint16_t db;
-    u32x4 q;
-    __builtin_memcpy(&db, p, 2);
-    __builtin_memcpy(&q, p + 2, 16);
+  __device__ static inline Scale scale(uint32_t bits) {
+    return Scale{__half2float(__ushort_as_half((uint16_t)bits)) * 0.0625f};
+  }
+  __device__ static inline void decode(const uint32_t *q, float u[32]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t v = q[i] ^ 0x88888888u;
@@ -109,7 +103,6 @@ template <> struct Fmt<QG_Q4_0> {
         u[16 + 4 * i + k] = (float)(int8_t)(hi >> (8 * k));
       }
     }
-    return Scale{__half2float(__ushort_as_half(db)) * 0.0625f};
   }
   __device__ static inline float apply(Scale s, float v) { return s.d16 * v; }
   __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d16, v, acc); }
@@ -121,26 +114,23 @@ template <> struct Fmt<QG_Q4_0> {
 // (scale 1.0: the E2M1 value itself, exact); the E8M0 scale is applied with an
 // exact ldexp, and e = 255 gives NaN.
 template <> struct Fmt<QG_MXFP4> {
-  static constexpr int kBytes = 17;
+  static constexpr int kBytes = 17, kScaleBytes = 1, kWords = 4;
   struct Scale { int e; };
+  __device__ static inline Scale scale(uint32_t bits) { return Scale{(int)(bits & 0xffu)}; }
   // f = (value of the byte's low nibble, value of its high nibble)
   template <typename V2>
-  __device__ static inline void unpack(uint32_t, V2 f, float *u) {
+  __device__ static inline void unpack(V2 f, float *u) {
     u[0] = f[0];
     u[16] = f[1];
   }
-  __device__ static inline Scale load(const uint8_t *p, float u[32]) {
-    u32x4 q;
-    const int e = p[0];
-    __builtin_memcpy(&q, p + 1, 16);
+  __device__ static inline void decode(const uint32_t *q, float u[32]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 0), u + 4 * i + 0);
-      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 1), u + 4 * i + 1);
-      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 2), u + 4 * i + 2);
-      unpack(q[i], __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 3), u + 4 * i + 3);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 0), u + 4 * i + 0);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 1), u + 4 * i + 1);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 2), u + 4 * i + 2);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 3), u + 4 * i + 3);
     }
-    return Scale{e};
   }
   __device__ static inline float apply(Scale s, float v) {
     return s.e == 255 ? __builtin_nanf("") : ldexpf(v, s.e - 127);
@@ -153,7 +143,7 @@ template <> struct Fmt<QG_MXFP4> {
 // ---------------------------------------------------------------------------
 
 struct WinDev {
-  const uint8_t *base;  // row 0 of the window's matrix
+  const uint8_t *base;  // row 0 of the window's matrix (16-byte aligned)
   const float *x;
   float *y;             // y[r - row_start] <-> row r
   int64_t row_start, row_end;
@@ -167,112 +157,211 @@ struct GemvArgs {
   int32_t n_win, nb, tile_rows, tiles_per_team, n_tiles;
 };
 
+// Sum over the 64 lanes of a wave in a fixed order (DPP row shifts, then row
+// broadcasts); the total lands in lane 63.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK,
+                                                               BANK_MASK, false));
+}
+
+__device__ __forceinline__ float wave_sum63(float v) {
+  v += dpp_f<0x111, 0xf, 0xf>(v);  // row_shr:1
+  v += dpp_f<0x112, 0xf, 0xf>(v);  // row_shr:2
+  v += dpp_f<0x114, 0xf, 0xe>(v);  // row_shr:4
+  v += dpp_f<0x118, 0xf, 0xc>(v);  // row_shr:8
+  v += dpp_f<0x142, 0xa, 0xf>(v);  // row_bcast:15
+  v += dpp_f<0x143, 0xc, 0xf>(v);  // row_bcast:31
+  return v;
+}
+
+// Same sum, every lane holding it (xor butterfly); used off the hot path.
 __device__ __forceinline__ float wave_sum(float v) {
-  // Fixed xor butterfly: every lane ends with the same, order-fixed sum.
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
+// Largest rows per tile, per (format, block columns per lane): the fetched
+// rows of a tile live in registers until staged, sized to the register budget.
+template <int FMT, int C> struct TileCap { static constexpr int value = 1; };
+template <> struct TileCap<QG_Q8_0, 1> { static constexpr int value = 6; };
+template <> struct TileCap<QG_Q8_0, 2> { static constexpr int value = 2; };
+template <> struct TileCap<QG_Q4_0, 1> { static constexpr int value = 8; };
+template <> struct TileCap<QG_Q4_0, 2> { static constexpr int value = 4; };
+template <> struct TileCap<QG_MXFP4, 1> { static constexpr int value = 8; };
+template <> struct TileCap<QG_MXFP4, 2> { static constexpr int value = 4; };
+
+// One team = WT waves.  Wave w owns the contiguous block columns
+// [w*64*C, (w+1)*64*C) of every row (its "slice"), lane l the columns
+// w*64*C + l + 64*c, whose 32 activations each it keeps in registers.
+// A tile is up to R rows of one row block.  Each wave fetches the slice bytes
+// of a tile's rows with coalesced, 16-byte aligned loads into registers (row
+// i's chunks always in buf[i]); row by row it stages them in its own LDS
+// buffer, reissues buf[i] for row i of the next tile, and reads its blocks
+// back (dword reads realigned with v_alignbyte, any byte alignment).  So a
+// wave keeps about R rows of weights in flight at all times.  The team's
+// per-wave row sums meet in LDS and are added in wave order.
 template <int FMT, int WT, int C>
-__global__ void __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(3)))
 gemv_kernel(const GemvArgs a) {
   using F = Fmt<FMT>;
-  constexpr int T = 64 * WT;
-  const int tl = threadIdx.x;
-  const int lane = tl & 63;
-  const int wave = tl >> 6;
+  constexpr int BB = F::kBytes;
+  constexpr int R = TileCap<FMT, C>::value;
+  constexpr int SB = 64 * C;                   // blocks per slice
+  constexpr int CH = (SB * BB + 15) / 16 + 1;  // 16-byte chunks a slice can touch
+  constexpr int V = (CH + 63) / 64;            // chunk loads per lane per row
+  constexpr int ROWB = 64 * V * 16 + 16;       // staged bytes per row, with read slack
+  __shared__ __attribute__((aligned(16))) uint8_t stage[WT][2][ROWB];
+  __shared__ float red[2][WT][R];
 
-  __shared__ float red[2][WT][kTileRowsMulti];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nb = a.nb;
+  const int64_t rb = a.row_bytes;
+  const int slice_b0 = wave * SB;
+  const int slice_n = max(0, min(SB, nb - slice_b0));  // >= 1 by the choice of WT
+  const int64_t slice_off = (int64_t)slice_b0 * BB;
+  const int slice_len = slice_n * BB;
 
   const int t_begin = blockIdx.x * a.tiles_per_team;
   const int t_end = min(t_begin + a.tiles_per_team, a.n_tiles);
-  const int nb = a.nb;
-  const int64_t rbytes = a.row_bytes;
+  if (t_begin >= t_end) return;
+
+  auto tile_rows = [&](int t, int &w, int64_t &r0, int64_t &r1) {
+    while (t >= a.tile_prefix[w + 1]) ++w;
+    const WinDev &W = a.win[w];
+    const int tt = t - a.tile_prefix[w];
+    const int tpb = (int)((a.block_rows + a.tile_rows - 1) / a.tile_rows);
+    const int blk = tt / tpb, tib = tt - blk * tpb;
+    r0 = W.row_start + (int64_t)blk * a.block_rows + (int64_t)tib * a.tile_rows;
+    r1 = min(r0 + a.tile_rows, min(W.row_start + (int64_t)(blk + 1) * a.block_rows, W.row_end));
+  };
+
+  // Fetch row i of a tile (rows past the tile's end re-read its last row, and
+  // chunks past the slice re-read its last chunk: every load stays in bounds
+  // and is unconditional, so the compiler can count them exactly).
+  u32x4 buf[R][V];
+  auto fetch_row = [&](int i, int w, int64_t r0, int64_t r1) {
+    const uint8_t *p = a.win[w].base + slice_off + min(r0 + i, r1 - 1) * rb;
+    const int ph = (int)((uintptr_t)p & 15);
+    const int last = (ph + slice_len - 1) >> 4;
+    const uint8_t *pa = p - ph;
+#pragma unroll
+    for (int v = 0; v < V; ++v) buf[i][v] = *(const u32x4 *)(pa + 16 * min(lane + 64 * v, last));
+  };
 
   float xr[C][32];
-  int cur = -1;
-  int w = 0;
+  int xw = -1;
+  auto load_x = [&](int w) {
+    const float *x = a.win[w].x;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = slice_b0 + lane + 64 * c;
+      const int jj = min(j, nb - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float4 v;
+        __builtin_memcpy(&v, x + 32 * jj + 4 * q, 16);
+        const bool ok = j < nb;
+        xr[c][4 * q + 0] = ok ? v.x : 0.0f;
+        xr[c][4 * q + 1] = ok ? v.y : 0.0f;
+        xr[c][4 * q + 2] = ok ? v.z : 0.0f;
+        xr[c][4 * q + 3] = ok ? v.w : 0.0f;
+      }
+    }
+  };
+
+  int t = t_begin, w = 0;
+  int64_t r0, r1;
+  tile_rows(t, w, r0, r1);
+#pragma unroll
+  for (int i = 0; i < R; ++i) fetch_row(i, w, r0, r1);
   int parity = 0;
-
-  for (int t = t_begin; t < t_end; ++t) {
-    while (t >= a.tile_prefix[w + 1]) ++w;
-    const WinDev W = a.win[w];
-    if (w != cur) {
-      cur = w;
+  for (;;) {
+    const int nt = t + 1;
+    int nw = w;
+    int64_t n0 = r0, n1 = r1;
+    const bool more = nt < t_end;
+    if (more) tile_rows(nt, nw, n0, n1);
+    if (w != xw) {
+      load_x(w);
+      xw = w;
+    }
+    const WinDev &W = a.win[w];
+    const int nrows = (int)(r1 - r0);
+    float acc[R];
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int j = tl + T * c;
-        if (j < nb) {
+    for (int i = 0; i < R; ++i) {
+      acc[i] = 0.0f;
+      // Stage row i (unconditionally: a row past the tile's end writes a
+      // buffer no later read uses), then reuse buf[i] for the next tile.
+      uint8_t *sb = stage[wave][i & 1];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            float4 v;
-            __builtin_memcpy(&v, W.x + 32 * j + 4 * q, 16);
-            xr[c][4 * q + 0] = v.x;
-            xr[c][4 * q + 1] = v.y;
-            xr[c][4 * q + 2] = v.z;
-            xr[c][4 * q + 3] = v.w;
-          }
-        } else {
+      for (int v = 0; v < V; ++v) *(u32x4 *)(sb + 16 * (lane + 64 * v)) = buf[i][v];
+      if (more) fetch_row(i, nw, n0, n1);
+      if (i < nrows) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int ph = (int)((uintptr_t)(W.base + slice_off + (r0 + i) * rb) & 15);
+        float s = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 32; ++e) xr[c][e] = 0.0f;
+        for (int c = 0; c < C; ++c) {
+          const int b = lane + 64 * c;
+          const int bo = ph + BB * b;  // block's byte offset in the staged row
+          uint32_t sbits;
+          if (F::kScaleBytes == 2)
+            sbits = *(const uint16_t *)(sb + bo);
+          else
+            sbits = sb[bo];
+          const int po = bo + F::kScaleBytes;  // payload byte offset
+          const int sh = po & 3;
+          const uint32_t *pw = (const uint32_t *)(sb + (po & ~3));
+          uint32_t raw[F::kWords + 1], q[F::kWords];
+#pragma unroll
+          for (int m = 0; m <= F::kWords; ++m) raw[m] = pw[m];
+#pragma unroll
+          for (int m = 0; m < F::kWords; ++m) q[m] = __builtin_amdgcn_alignbyte(raw[m + 1], raw[m], sh);
+          float u[32];
+          F::decode(q, u);
+          float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
+          const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
+          s = b < slice_n ? blk_acc : s;
         }
+        acc[i] = wave_sum63(s);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
-    // tile -> rows [r0, r1), never across a row block
-    const int64_t tt = t - a.tile_prefix[w];
-    const int64_t B = a.block_rows;
-    const int64_t tpb = (B + a.tile_rows - 1) / a.tile_rows;
-    const int64_t blk = tt / tpb, tib = tt - blk * tpb;
-    const int64_t r0 = W.row_start + blk * B + tib * a.tile_rows;
-    int64_t r1 = r0 + a.tile_rows;
-    r1 = min(r1, W.row_start + (blk + 1) * B);
-    r1 = min(r1, W.row_end);
-
-    for (int64_t r = r0; r < r1; r += 2) {
-      const bool two = (r + 1 < r1);
-      const uint8_t *row0 = W.base + r * rbytes;
-      const uint8_t *row1 = two ? row0 + rbytes : row0;
-      float acc0 = 0.0f, acc1 = 0.0f;
+    if (WT == 1) {
+      if (lane == 63) {
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int j = tl + T * c;
-        if (j < nb) {
-          float u0[32], u1[32];
-          const auto s0 = F::load(row0 + (int64_t)F::kBytes * j, u0);
-          const auto s1 = F::load(row1 + (int64_t)F::kBytes * j, u1);
-          float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < R; ++i)
+          if (i < nrows) W.y[r0 + i - W.row_start] = acc[i];
+      }
+    } else {
+      if (lane == 63) {
 #pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            p0[e & 3] = fmaf(u0[e], xr[c][e], p0[e & 3]);
-            p1[e & 3] = fmaf(u1[e], xr[c][e], p1[e & 3]);
-          }
-          acc0 = F::fma_acc(s0, (p0[0] + p0[1]) + (p0[2] + p0[3]), acc0);
-          acc1 = F::fma_acc(s1, (p1[0] + p1[1]) + (p1[2] + p1[3]), acc1);
-        }
+        for (int i = 0; i < R; ++i) red[parity][wave][i] = acc[i];
       }
-      acc0 = wave_sum(acc0);
-      acc1 = wave_sum(acc1);
-      if (WT == 1) {
-        if (lane == 0) W.y[r - W.row_start] = acc0;
-        if (lane == 1 && two) W.y[r + 1 - W.row_start] = acc1;
-      } else {
-        const int i = (int)(r - r0);
-        if (lane == 0) red[parity][wave][i] = acc0;
-        if (lane == 1 && two) red[parity][wave][i + 1] = acc1;
-      }
-    }
-    if (WT > 1) {
       __syncthreads();
-      const int n = (int)(r1 - r0);
-      if (tl < n) {
-        float s = red[parity][0][tl];
+      if ((int)threadIdx.x < nrows) {
+        float s = red[parity][0][threadIdx.x];
 #pragma unroll
-        for (int v = 1; v < WT; ++v) s += red[parity][v][tl];
-        W.y[r0 + tl - W.row_start] = s;
+        for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
+        W.y[r0 + threadIdx.x - W.row_start] = s;
       }
       parity ^= 1;
     }
+    if (!more) break;
+    t = nt;
+    w = nw;
+    r0 = n0;
+    r1 = n1;
   }
 }
 
@@ -288,8 +377,13 @@ __global__ void dequant_kernel(const uint8_t *base, int64_t row_start, int64_t n
   if (id >= n_rows * nb) return;
   const int64_t r = id / nb;
   const int j = (int)(id - r * nb);
+  const uint8_t *p = base + (row_start + r) * row_bytes + (int64_t)F::kBytes * j;
+  uint32_t sbits = 0, q[F::kWords];
+  __builtin_memcpy(&sbits, p, F::kScaleBytes);
+  __builtin_memcpy(q, p + F::kScaleBytes, 4 * F::kWords);
   float u[32];
-  const auto s = F::load(base + (row_start + r) * row_bytes + (int64_t)F::kBytes * j, u);
+  F::decode(q, u);
+  const auto s = F::scale(sbits);
   float *o = out + r * (int64_t)nb * 32 + 32 * j;
 #pragma unroll
   for (int e = 0; e < 32; ++e) o[e] = F::apply(s, u[e]);
@@ -363,13 +457,24 @@ int check_fmt_k(int32_t fmt, int64_t k) {
 
 // Team shape (WT waves, C block columns per lane) -- a function of k only.
 struct Shape { int wt, c; };
+// Team shape, a function of k only: one block column per lane while a row
+// fits 12 waves (k <= 24576), else two; the team has one wave per 64*C
+// columns, so every wave owns at least one block.
 int team_shape(int64_t k, Shape *s) {
   const int64_t nb = k / 32;
-  for (int wt = 1; wt <= kMaxWT; wt *= 2) {
-    const int64_t c = (nb + 64 * wt - 1) / (64 * wt);
-    if (c <= kMaxC) { s->wt = wt; s->c = (int)c; return QG_OK; }
+  for (int c = 1; c <= kMaxC; ++c) {
+    const int64_t wt = (nb + 64 * c - 1) / (64 * c);
+    if (wt <= kMaxWT) { s->wt = (int)wt; s->c = c; return QG_OK; }
   }
-  return QG_E_SHAPE;  // k above 64 * kMaxWT * kMaxC * 32 = 65536
+  return QG_E_SHAPE;  // k above 32 * 64 * kMaxWT * kMaxC = 49152
+}
+
+int tile_cap(int32_t fmt, int c) {
+  switch (fmt) {
+    case QG_Q8_0: return c == 1 ? TileCap<QG_Q8_0, 1>::value : TileCap<QG_Q8_0, 2>::value;
+    case QG_Q4_0: return c == 1 ? TileCap<QG_Q4_0, 1>::value : TileCap<QG_Q4_0, 2>::value;
+    default: return c == 1 ? TileCap<QG_MXFP4, 1>::value : TileCap<QG_MXFP4, 2>::value;
+  }
 }
 
 int check_matrix(const qg_matrix *w) {
@@ -381,6 +486,7 @@ int check_matrix(const qg_matrix *w) {
   if ((rc = team_shape(w->k, &s))) return rc;
   if (w->n_bytes != w->n_rows * (w->k / 32) * block_bytes(w->fmt)) return QG_E_SIZE;
   if (!w->data && w->n_bytes > 0) return QG_E_NULL;
+  if ((uintptr_t)w->data & 15) return QG_E_ARG;
   return QG_OK;
 }
 
@@ -405,74 +511,96 @@ int device_cus() {
 
 typedef void (*GemvFn)(GemvArgs);
 
-template <int FMT, int WT>
-GemvFn pick_c(int c) {
-  switch (c) {
-    case 1: return gemv_kernel<FMT, WT, 1>;
-    case 2: return gemv_kernel<FMT, WT, 2>;
-    case 3: return gemv_kernel<FMT, WT, 3>;
-    default: return gemv_kernel<FMT, WT, 4>;
-  }
+template <int FMT, int C, int... WT>
+GemvFn pick_wt(int wt, std::integer_sequence<int, WT...>) {
+  GemvFn fn = nullptr;
+  ((wt == WT + 1 ? (fn = gemv_kernel<FMT, WT + 1, C>, 0) : 0), ...);
+  return fn;
 }
 
 template <int FMT>
-GemvFn pick_wt(int wt, int c) {
-  switch (wt) {
-    case 1: return pick_c<FMT, 1>(c);
-    case 2: return pick_c<FMT, 2>(c);
-    case 4: return pick_c<FMT, 4>(c);
-    default: return pick_c<FMT, 8>(c);
-  }
+GemvFn pick_fmt(Shape s) {
+  if (s.c == 1) return pick_wt<FMT, 1>(s.wt, std::make_integer_sequence<int, kMaxWT>{});
+  return pick_wt<FMT, 2>(s.wt, std::make_integer_sequence<int, kMaxWT>{});
 }
 
 GemvFn pick(int32_t fmt, Shape s) {
   switch (fmt) {
-    case QG_Q8_0: return pick_wt<QG_Q8_0>(s.wt, s.c);
-    case QG_Q4_0: return pick_wt<QG_Q4_0>(s.wt, s.c);
-    default: return pick_wt<QG_MXFP4>(s.wt, s.c);
+    case QG_Q8_0: return pick_fmt<QG_Q8_0>(s);
+    case QG_Q4_0: return pick_fmt<QG_Q4_0>(s);
+    default: return pick_fmt<QG_MXFP4>(s);
   }
+}
+
+// Tiles of n windows with tile_rows rows each, never across a row block of B.
+int64_t count_tiles(const qg_window *win, int n, int64_t B, int tile_rows) {
+  int64_t tiles = 0;
+  const int64_t tpb = (B + tile_rows - 1) / tile_rows;
+  for (int i = 0; i < n; ++i) {
+    const int64_t len = win[i].row_end - win[i].row_start;
+    const int64_t full = len / B, rem = len - full * B;
+    tiles += full * tpb + (rem + tile_rows - 1) / tile_rows;
+  }
+  return tiles;
 }
 
 // Launch one grid over n windows (already validated).  win[i].data is the
 // device address of the window's matrix row 0.
-int launch_gemv(int32_t fmt, int64_t k, const qg_window *win, int n, int64_t block_rows,
+//
+// Work split (it never changes a row's result): the grid has at most
+// CUs * 12 / WT teams (3 waves per SIMD); tiles hold tile_rows <= R rows, and
+// tile_rows is picked to minimise the rows the busiest team walks, with a
+// small charge per tile.
+int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
                 hipStream_t stream) {
   Shape s;
   int rc = team_shape(k, &s);
   if (rc) return rc;
+  qg_window win[kMaxWindows];
+  int n = 0;
+  int64_t maxlen = 1;
+  for (int i = 0; i < n_in; ++i) {
+    if (win_in[i].row_end == win_in[i].row_start) continue;
+    win[n++] = win_in[i];
+    maxlen = std::max<int64_t>(maxlen, win_in[i].row_end - win_in[i].row_start);
+  }
+  if (n == 0) return QG_OK;
+  const int64_t B = block_rows > 0 ? std::min<int64_t>(block_rows, maxlen) : maxlen;
+  const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * 12 / s.wt);
+  const int cap = tile_cap(fmt, s.c);
+  int best_tr = 1;
+  double best_cost = 1e300;
+  for (int tr = 1; tr <= cap; ++tr) {
+    const int64_t tiles = count_tiles(win, n, B, tr);
+    const int64_t teams = std::min(teams_max, tiles);
+    const int64_t tpt = (tiles + teams - 1) / teams;
+    const double cost = (double)tpt * tr + 0.5 * (double)tpt;
+    if (cost < best_cost - 1e-9) { best_cost = cost; best_tr = tr; }
+  }
+  const int tile_rows = best_tr;
   GemvArgs a;
   memset(&a, 0, sizeof(a));
-  const int tile_rows = s.wt == 1 ? 2 : kTileRowsMulti;
-  int64_t maxlen = 1;
-  for (int i = 0; i < n; ++i) maxlen = std::max<int64_t>(maxlen, win[i].row_end - win[i].row_start);
-  const int64_t B = block_rows > 0 ? block_rows : maxlen;
   int64_t tiles = 0;
-  int m = 0;
+  const int64_t tpb = (B + tile_rows - 1) / tile_rows;
   for (int i = 0; i < n; ++i) {
     const int64_t len = win[i].row_end - win[i].row_start;
-    if (len == 0) continue;
-    const int64_t tpb = (B + tile_rows - 1) / tile_rows;
     const int64_t full = len / B, rem = len - full * B;
-    a.win[m].base = (const uint8_t *)win[i].data;
-    a.win[m].x = win[i].x;
-    a.win[m].y = win[i].y;
-    a.win[m].row_start = win[i].row_start;
-    a.win[m].row_end = win[i].row_end;
-    a.tile_prefix[m] = (int32_t)tiles;
+    a.win[i].base = (const uint8_t *)win[i].data;
+    a.win[i].x = win[i].x;
+    a.win[i].y = win[i].y;
+    a.win[i].row_start = win[i].row_start;
+    a.win[i].row_end = win[i].row_end;
+    a.tile_prefix[i] = (int32_t)tiles;
     tiles += full * tpb + (rem + tile_rows - 1) / tile_rows;
-    ++m;
+    if (tiles > INT32_MAX / 2) return QG_E_SHAPE;
   }
-  if (m == 0) return QG_OK;
-  if (tiles > INT32_MAX / 2) return QG_E_SHAPE;
-  a.tile_prefix[m] = (int32_t)tiles;
-  for (int i = m + 1; i <= kMaxWindows; ++i) a.tile_prefix[i] = (int32_t)tiles;
-  a.n_win = m;
+  for (int i = n; i <= kMaxWindows; ++i) a.tile_prefix[i] = (int32_t)tiles;
+  a.n_win = n;
   a.nb = (int32_t)(k / 32);
   a.row_bytes = (k / 32) * block_bytes(fmt);
   a.block_rows = B;
   a.tile_rows = tile_rows;
   a.n_tiles = (int32_t)tiles;
-  const int64_t teams_max = (int64_t)device_cus() * 8 / s.wt;
   int64_t teams = std::min<int64_t>(teams_max, tiles);
   const int64_t tpt = (tiles + teams - 1) / teams;
   teams = (tiles + tpt - 1) / tpt;
@@ -493,6 +621,7 @@ int validate_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win
     if (win[i].n_rows < 0) return QG_E_SHAPE;
     if ((rc = check_range(win[i].n_rows, win[i].row_start, win[i].row_end))) return rc;
     if (win[i].row_end > win[i].row_start && (!win[i].data || !win[i].x || !win[i].y)) return QG_E_NULL;
+    if ((uintptr_t)win[i].data & 15) return QG_E_ARG;
   }
   return QG_OK;
 }
@@ -506,6 +635,7 @@ int validate_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win
 struct qg_streamer {
   int device;
   int64_t slot_bytes;
+  int64_t slot_stride;  // slot_bytes rounded up to 256 (slots stay 16-byte aligned)
   int lookahead;
   uint8_t *ring;
   hipStream_t copy;
@@ -523,10 +653,10 @@ const char *qgemv_strerror(int status) {
     case QG_OK: return "ok";
     case QG_E_NULL: return "a required pointer is NULL";
     case QG_E_FMT: return "unknown quantization format";
-    case QG_E_SHAPE: return "bad shape (k must be a positive multiple of 32, at most 65536; n_rows >= 0)";
+    case QG_E_SHAPE: return "bad shape (k must be a positive multiple of 32, at most 49152; n_rows >= 0)";
     case QG_E_RANGE: return "row range or expert id out of range";
     case QG_E_SIZE: return "n_bytes does not match n_rows * (k/32) * block bytes";
-    case QG_E_ARG: return "bad argument (block_rows, lookahead, window count, n, eps or stride)";
+    case QG_E_ARG: return "bad argument (block_rows, lookahead, window count, n, eps, stride, or weights not 16-byte aligned)";
     case QG_E_NOT_PINNED: return "streamed weights are not in page-locked host memory";
     case QG_E_CAPACITY: return "a row block is larger than a ring slot";
     case QG_E_HIP: return "HIP runtime error";
@@ -654,6 +784,7 @@ int qgemv_stream_create(int64_t slot_bytes, int32_t lookahead, qg_streamer **out
   *out = nullptr;
   qg_streamer *st = new qg_streamer();
   st->slot_bytes = slot_bytes;
+  st->slot_stride = (slot_bytes + 255) / 256 * 256;
   st->lookahead = lookahead;
   st->ring = nullptr;
   st->copy = nullptr;
@@ -666,7 +797,7 @@ int qgemv_stream_create(int64_t slot_bytes, int32_t lookahead, qg_streamer **out
   };
   hipError_t e;
   if ((e = hipGetDevice(&st->device)) != hipSuccess) return fail(e, "hipGetDevice");
-  if ((e = hipMalloc((void **)&st->ring, (size_t)slot_bytes * n)) != hipSuccess) return fail(e, "hipMalloc(ring)");
+  if ((e = hipMalloc((void **)&st->ring, (size_t)st->slot_stride * n)) != hipSuccess) return fail(e, "hipMalloc(ring)");
   if ((e = hipStreamCreateWithFlags(&st->copy, hipStreamNonBlocking)) != hipSuccess)
     return fail(e, "hipStreamCreateWithFlags");
   st->ready.assign(n, nullptr);
@@ -740,7 +871,7 @@ int stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win
     for (int64_t r = win[i].row_start; r < win[i].row_end; r += B) {
       const int64_t n = std::min(B, win[i].row_end - r);
       const int slot = (int)(st->next++ % (uint64_t)nslot);
-      uint8_t *dst = st->ring + (int64_t)slot * st->slot_bytes;
+      uint8_t *dst = st->ring + (int64_t)slot * st->slot_stride;
       if (st->freed_valid[slot]) QG_HIP(hipStreamWaitEvent(st->copy, st->freed[slot], 0));
       QG_HIP(hipMemcpyAsync(dst, (const uint8_t *)win[i].data + r * rb, (size_t)(n * rb),
                             hipMemcpyHostToDevice, st->copy));

@@ -83,7 +83,8 @@ def test_qgemv_rows_validation():
     assert rows_call(None) == E_NULL
     assert rows_call(mat(fmt=5)) == E_FMT
     assert rows_call(mat(k=48, nbytes=0)) == E_SHAPE
-    assert rows_call(mat(k=65536 + 32)) == E_SHAPE
+    assert rows_call(mat(k=49152 + 32)) == E_SHAPE
+    assert rows_call(mat(data=FAKE + 8)) == E_ARG  # not 16-byte aligned
     assert rows_call(mat(nbytes=8 * 2 * 34 - 1)) == E_SIZE
     assert rows_call(mat(nbytes=8 * 2 * 34 + 1)) == E_SIZE
     assert rows_call(mat(), r0=-1) == E_RANGE
