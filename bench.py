@@ -1,0 +1,331 @@
+"""Benchmark of the batch-1 dequant-GEMV path on one MI355X.
+
+Default workload: the full decode weight pass of a synthetic 20B-class dense
+model, Q8_0, 44 layers, hidden 6144, FFN 24576 (per layer QKV 18432x6144,
+out 6144x6144, up 24576x6144, down 6144x24576; 21.18 GB resident in HBM).  A
+step is one token: the 176 GEMVs of the pass, in order, each fed by the RMS
+carry of the previous one (the attention over a single position returns V, so
+the carry after QKV is the RMS-normalised V third).  Weights are random-init
+synthetic blocks; nothing is cached or skipped between tokens.
+
+Printed: one JSON line with the headline metric (effective weight GB/s of the
+whole timed region = weight bytes read / wall time), the roofline of the
+dominant kernel (its launches timed with HIP events on the launch stream), the
+CPU oracle timed on a bounded sample of the same pass, and a sampled parity
+check of the GPU results against the oracle.
+
+Other workloads (--workload): q4_0_4096, moe_mxfp4, ffn_streamed, q8_0_256.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "effective weight GB/s (% of HBM peak) of dequant-GEMV; decode tokens/s equiv"
+HBM_PEAK_GBS = 8000.0
+TOL = 1e-4
+
+
+def threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", 0) or min(16, os.cpu_count() or 1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# --- the dense decode pass -------------------------------------------------------
+
+class DensePass:
+    """Weights, buffers and prepared C-ABI calls of the synthetic dense model."""
+
+    def __init__(self, layers, hidden, ffn, dev, eps=1e-6, verbose=True):
+        import torch
+        import quantized_gemv_gguf_amd as q
+        self.q, self.torch = q, torch
+        self.L, self.H, self.F, self.dev, self.eps = layers, hidden, ffn, dev, eps
+        self.shapes = synth.dense_layer_shapes(hidden, ffn)
+        self.lib = q.lib()
+        self.stream = torch.cuda.current_stream().cuda_stream
+        t0 = time.time()
+        maxbytes = max(r * (k // 32) * 34 for _, r, k in self.shapes)
+        staging = torch.empty(maxbytes, dtype=torch.uint8, pin_memory=True)
+        self.w = []  # [layer][matrix] device tensors
+        for l in range(layers):
+            row = []
+            for m, (_, r, k) in enumerate(self.shapes):
+                nbytes = r * (k // 32) * 34
+                view = staging[:nbytes].numpy().reshape(r, (k // 32) * 34)
+                synth.blocks(synth.Q8_0, r, k, self.seed(l, m), out=view, threads=threads())
+                t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+                t.copy_(staging[:nbytes], non_blocking=False)
+                row.append(t)
+            self.w.append(row)
+            if verbose and (l % 11 == 10 or l == layers - 1):
+                print(f"[bench] generated {l + 1}/{layers} layers ({time.time() - t0:.1f}s)", file=sys.stderr,
+                      flush=True)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.qkv = torch.empty(3 * hidden, **f32)
+        self.o = torch.empty(hidden, **f32)
+        self.u = torch.empty(ffn, **f32)
+        self.a = torch.empty(ffn, **f32)
+        self.d = torch.empty(hidden, **f32)
+        self.c = torch.empty(hidden, **f32)
+        self.x0 = torch.from_numpy(synth.x_vec(hidden, synth.seed_of(5, 999))).to(dev)
+        # prepared calls: (matrix struct, rows, x ptr, y ptr, bytes, k)
+        ins = [self.c, self.c, self.c, self.a]
+        outs = [self.qkv, self.o, self.u, self.d]
+        self.mats, self.calls = [], []
+        for l in range(layers):
+            for m, (_, r, k) in enumerate(self.shapes):
+                cm = q.qg_matrix(self.w[l][m].data_ptr(), q.Q8_0, 0, r, k, self.w[l][m].numel())
+                self.mats.append(cm)
+                self.calls.append((ctypes.byref(cm), r, ins[m].data_ptr(), outs[m].data_ptr(),
+                                   self.w[l][m].numel(), k, m))
+        self.v_ptr = self.qkv.data_ptr() + 4 * 2 * hidden  # the V third of QKV
+        self.bytes_per_token = sum(c[4] for c in self.calls)
+
+    @staticmethod
+    def seed(layer, m):
+        return synth.seed_of(5, 4 * layer + m)
+
+    def reset(self):
+        """c = rms(x0): the carry the first token starts from."""
+        rc = self.lib.qgemv_rms_carry(self.x0.data_ptr(), self.c.data_ptr(), self.H, self.eps, 0, self.stream)
+        assert rc == 0
+
+    def token(self, events=None, hook=None):
+        """One token's pass.  events: list of (start, end) torch events, one
+        pair per GEMV, recorded around it on the launch stream."""
+        L = self.lib
+        H, F, st, eps = self.H, self.F, self.stream, self.eps
+        carry = [(self.v_ptr, self.c.data_ptr(), H, 0), (self.o.data_ptr(), self.c.data_ptr(), H, 0),
+                 (self.u.data_ptr(), self.a.data_ptr(), F, 1), (self.d.data_ptr(), self.c.data_ptr(), H, 0)]
+        for i, (mp, r, xp, yp, nbytes, k, m) in enumerate(self.calls):
+            if events is not None:
+                events[i][0].record()
+            rc = L.qgemv_rows(mp, 0, r, xp, yp, 0, st)
+            if events is not None:
+                events[i][1].record()
+            if rc != 0:
+                raise RuntimeError(f"qgemv_rows failed: {rc}")
+            if hook is not None:
+                hook(i, m)
+            vp, op, n, g = carry[m]
+            rc = L.qgemv_rms_carry(vp, op, n, eps, g, st)
+            if rc != 0:
+                raise RuntimeError(f"qgemv_rms_carry failed: {rc}")
+
+
+def dense_workload(args, dev):
+    import torch
+    c = synth.CONFIGS[5]
+    layers = args.layers or c["layers"]
+    model = DensePass(layers, c["hidden"], c["ffn"], dev)
+    torch.cuda.synchronize()
+    model.reset()
+    for _ in range(args.warmup):
+        model.token()
+    torch.cuda.synchronize()
+    n = len(model.calls)
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+              for _ in range(args.steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    for s in range(args.steps):
+        model.token(events[s])
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = g0.elapsed_time(g1)
+    # per-launch durations, grouped by kernel variant (k decides the variant)
+    per_k = {}
+    for s in range(args.steps):
+        for i, (mp, r, xp, yp, nbytes, k, m) in enumerate(model.calls):
+            ms = events[s][i][0].elapsed_time(events[s][i][1])
+            e = per_k.setdefault(k, [0, 0.0, 0])
+            e[0] += nbytes
+            e[1] += ms
+            e[2] += 1
+    total_bytes = model.bytes_per_token * args.steps
+    gbs = total_bytes / wall / 1e9
+    kernels = {}
+    for k, (b, ms, cnt) in sorted(per_k.items()):
+        kernels[f"gemv_q8_0_k{k}"] = {"launches": cnt, "avg_us": ms / cnt * 1e3, "avg_bytes": b / cnt,
+                                      "GBs": b / (ms / 1e3) / 1e9}
+    dom_k = max(per_k, key=lambda k: per_k[k][1])
+    b, ms, cnt = per_k[dom_k]
+    achieved = b / (ms / 1e3) / 1e9
+    res = {
+        "value": gbs,
+        "ms_per_step": wall / args.steps * 1e3,
+        "tokens_per_s": args.steps / wall,
+        "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "gpu_event_ms_per_step": gpu_ms / args.steps,
+        "bytes_per_token": model.bytes_per_token,
+        "config": {"workload": c["name"], "layers": layers, "hidden": c["hidden"], "ffn": c["ffn"],
+                   "format": "Q8_0", "tokens": args.steps, "gemvs_per_token": n,
+                   "weight_bytes_per_token": model.bytes_per_token},
+        "roofline": {"bound": "hbm", "kernel": f"gemv_q8_0_k{dom_k}", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_us": ms / cnt * 1e3, "bytes_per_launch": b / cnt},
+        "kernels": kernels,
+    }
+    # identity: tokens/s = bandwidth / active bytes per token
+    assert abs(res["tokens_per_s"] - gbs * 1e9 / model.bytes_per_token) <= 1e-9 * res["tokens_per_s"]
+    if not args.no_check:
+        res["parity"] = dense_parity(model, layers)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = dense_cpu_baseline(model, args.cpu_seconds)
+    return res
+
+
+def dense_parity(model, layers, n_rows=48, seed=7):
+    """Teacher-forced check of sampled rows of every GEMV of layers 0 and
+    layers-1 (their inputs and outputs copied back), against the oracle on
+    weight rows regenerated on the host."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(seed)
+    want = {0, 1, 2, 3, 4 * (layers - 1), 4 * (layers - 1) + 1, 4 * (layers - 1) + 2, 4 * (layers - 1) + 3}
+    ins = [model.c, model.c, model.c, model.a]
+    outs = [model.qkv, model.o, model.u, model.d]
+    worst_n, worst_c = 0.0, 0.0
+    checked = 0
+
+    def hook(i, m):
+        nonlocal worst_n, worst_c, checked
+        if i not in want:
+            return
+        torch.cuda.synchronize()
+        x = ins[m].cpu().numpy()
+        y = outs[m].cpu().numpy().astype(np.float64)
+        _, r, k = model.shapes[m]
+        rows = np.sort(rng.choice(r, n_rows, replace=False))
+        ref, a = np.empty(n_rows), np.empty(n_rows)
+        for j, row in enumerate(rows):
+            wrow = synth.blocks(synth.Q8_0, r, k, model.seed(i // 4, m), r0=int(row), r1=int(row) + 1, threads=1)
+            ref[j], a[j] = [v[0] for v in oracle.gemv_rows(oracle.Q8_0, wrow, 1, k, x, threads=1)]
+        err = np.abs(y[rows] - ref)
+        worst_c = max(worst_c, float(np.max(err / a)))
+        worst_n = max(worst_n, float(err.max() / np.abs(ref).max()))
+        checked += n_rows
+
+    model.token(hook=hook)
+    torch.cuda.synchronize()
+    ok = worst_c <= TOL and worst_n <= TOL
+    return {"rows_checked": checked, "max_componentwise": worst_c, "max_normwise_sampled": worst_n,
+            "tol": TOL, "pass": bool(ok)}
+
+
+def dense_cpu_baseline(model, seconds):
+    """The oracle (fp64, all threads) on the same pass, layer by layer from
+    token 0's carry, until `seconds` of oracle time have run."""
+    import oracle
+    t_oracle = 0.0
+    nbytes = 0
+    nth = threads()
+    c = oracle.rms_carry(synth.x_vec(model.H, synth.seed_of(5, 999)).astype(np.float64), model.eps)
+    done = 0
+    for l in range(model.L):
+        ws = [synth.blocks(synth.Q8_0, r, k, model.seed(l, m), threads=nth) for m, (_, r, k) in enumerate(model.shapes)]
+        t = time.perf_counter()
+        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
+        c = oracle.rms_carry(y[2 * model.H:3 * model.H], model.eps)
+        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[1], *model.shapes[1][1:], c.astype(np.float32), threads=nth)
+        c = oracle.rms_carry(y, model.eps)
+        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[2], *model.shapes[2][1:], c.astype(np.float32), threads=nth)
+        act = oracle.rms_carry(y, model.eps, gelu=True)
+        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[3], *model.shapes[3][1:], act.astype(np.float32), threads=nth)
+        c = oracle.rms_carry(y, model.eps)
+        t_oracle += time.perf_counter() - t
+        nbytes += sum(w.nbytes for w in ws)
+        done += 1
+        if t_oracle >= seconds:
+            break
+    gbs = nbytes / t_oracle / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "tokens_per_s_equiv": gbs * 1e9 / model.bytes_per_token,
+            "sample": f"token 0, layers 0..{done - 1} of {model.L} ({4 * done} GEMVs, {nbytes / 1e9:.2f} GB), "
+                      f"fp64 scalar C oracle, {nth} threads, {t_oracle:.1f} s",
+            "cpu": cpu_model()}
+
+
+WORKLOADS = {"dense20b": dense_workload}
+
+
+# --- entry --------------------------------------------------------------------------
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=32)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="dense20b",
+                   choices=sorted(WORKLOADS))
+    p.add_argument("--layers", type=int, default=0, help="fewer layers for a quick run (not a valid headline)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run a 256 MiB device-to-device copy (a kernel of known traffic, to scale HBM counters)")
+    args = p.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is a design note, not built)", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    fn = WORKLOADS[args.workload]
+    res = fn(args, dev)
+    line = {
+        "metric": METRIC,
+        "value": round(res.pop("value"), 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res.pop("ms_per_step"), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+    }
+    line.update(res)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -216,7 +216,7 @@ gemv_kernel(const GemvArgs a) {
   __shared__ float red[2][WT][R];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int nb = a.nb;
   const int64_t rb = a.row_bytes;
   const int slice_b0 = wave * SB;
@@ -228,33 +228,51 @@ gemv_kernel(const GemvArgs a) {
   const int t_end = min(t_begin + a.tiles_per_team, a.n_tiles);
   if (t_begin >= t_end) return;
 
-  auto tile_rows = [&](int t, int &w, int64_t &r0, int64_t &r1) {
+  // Kernel-argument fields used in the loop are read once into registers:
+  // a scalar reload inside the loop would wait on the LDS counter too.
+  const int64_t B = a.block_rows;
+  const int TR = a.tile_rows;
+  const int tpb = (int)((B + TR - 1) / TR);
+  struct Tile {
+    int w;
+    int64_t r0, r1, row_start;
+    const uint8_t *base;
+    const float *x;
+    float *y;
+  };
+  auto locate = [&](int t, int w0, Tile &T) {
+    int w = w0;
     while (t >= a.tile_prefix[w + 1]) ++w;
-    const WinDev &W = a.win[w];
     const int tt = t - a.tile_prefix[w];
-    const int tpb = (int)((a.block_rows + a.tile_rows - 1) / a.tile_rows);
     const int blk = tt / tpb, tib = tt - blk * tpb;
-    r0 = W.row_start + (int64_t)blk * a.block_rows + (int64_t)tib * a.tile_rows;
-    r1 = min(r0 + a.tile_rows, min(W.row_start + (int64_t)(blk + 1) * a.block_rows, W.row_end));
+    T.w = w;
+    T.row_start = a.win[w].row_start;
+    T.base = a.win[w].base;
+    T.x = a.win[w].x;
+    T.y = a.win[w].y;
+    T.r0 = T.row_start + (int64_t)blk * B + (int64_t)tib * TR;
+    T.r1 = min(T.r0 + TR, min(T.row_start + (int64_t)(blk + 1) * B, a.win[w].row_end));
   };
 
   // Fetch row i of a tile (rows past the tile's end re-read its last row, and
   // chunks past the slice re-read its last chunk: every load stays in bounds
   // and is unconditional, so the compiler can count them exactly).
   u32x4 buf[R][V];
-  auto fetch_row = [&](int i, int w, int64_t r0, int64_t r1) {
-    const uint8_t *p = a.win[w].base + slice_off + min(r0 + i, r1 - 1) * rb;
-    const int ph = (int)((uintptr_t)p & 15);
-    const int last = (ph + slice_len - 1) >> 4;
+  // The row address, its phase and the last chunk are wave-uniform (scalar);
+  // a lane adds only its 32-bit chunk offset.
+  const uint32_t lane16 = 16u * lane;
+  auto fetch_row = [&](int i, const Tile &T) {
+    const uint8_t *p = T.base + slice_off + min(T.r0 + i, T.r1 - 1) * rb;
+    const uint32_t ph = (uint32_t)((uintptr_t)p & 15);
+    const uint32_t last16 = ((ph + (uint32_t)slice_len - 1) >> 4) << 4;
     const uint8_t *pa = p - ph;
 #pragma unroll
-    for (int v = 0; v < V; ++v) buf[i][v] = *(const u32x4 *)(pa + 16 * min(lane + 64 * v, last));
+    for (int v = 0; v < V; ++v) buf[i][v] = *(const u32x4 *)(pa + min(lane16 + 1024u * v, last16));
   };
 
   float xr[C][32];
   int xw = -1;
-  auto load_x = [&](int w) {
-    const float *x = a.win[w].x;
+  auto load_x = [&](const float *x) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int j = slice_b0 + lane + 64 * c;
@@ -272,24 +290,21 @@ gemv_kernel(const GemvArgs a) {
     }
   };
 
-  int t = t_begin, w = 0;
-  int64_t r0, r1;
-  tile_rows(t, w, r0, r1);
+  int t = t_begin;
+  Tile cur, nxt;
+  locate(t, 0, cur);
 #pragma unroll
-  for (int i = 0; i < R; ++i) fetch_row(i, w, r0, r1);
+  for (int i = 0; i < R; ++i) fetch_row(i, cur);
   int parity = 0;
   for (;;) {
-    const int nt = t + 1;
-    int nw = w;
-    int64_t n0 = r0, n1 = r1;
-    const bool more = nt < t_end;
-    if (more) tile_rows(nt, nw, n0, n1);
-    if (w != xw) {
-      load_x(w);
-      xw = w;
+    const bool more = t + 1 < t_end;
+    nxt = cur;
+    if (more) locate(t + 1, cur.w, nxt);
+    if (cur.w != xw) {
+      load_x(cur.x);
+      xw = cur.w;
     }
-    const WinDev &W = a.win[w];
-    const int nrows = (int)(r1 - r0);
+    const int nrows = (int)(cur.r1 - cur.r0);
     float acc[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -298,31 +313,23 @@ gemv_kernel(const GemvArgs a) {
       // buffer no later read uses), then reuse buf[i] for the next tile.
       uint8_t *sb = stage[wave][i & 1];
 #pragma unroll
-      for (int v = 0; v < V; ++v) *(u32x4 *)(sb + 16 * (lane + 64 * v)) = buf[i][v];
-      if (more) fetch_row(i, nw, n0, n1);
+      for (int v = 0; v < V; ++v) *(u32x4 *)(sb + lane16 + 1024 * v) = buf[i][v];
+      if (more) fetch_row(i, nxt);
       if (i < nrows) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        // Other lanes' staged bytes are read below: keep the order (LDS
+        // operations of one wave complete in order).
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int ph = (int)((uintptr_t)(W.base + slice_off + (r0 + i) * rb) & 15);
+        const int ph = (int)((uintptr_t)(cur.base + slice_off + (cur.r0 + i) * rb) & 15);
         float s = 0.0f;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           const int b = lane + 64 * c;
           const int bo = ph + BB * b;  // block's byte offset in the staged row
-          uint32_t sbits;
-          if (F::kScaleBytes == 2)
-            sbits = *(const uint16_t *)(sb + bo);
-          else
-            sbits = sb[bo];
-          const int po = bo + F::kScaleBytes;  // payload byte offset
-          const int sh = po & 3;
-          const uint32_t *pw = (const uint32_t *)(sb + (po & ~3));
-          uint32_t raw[F::kWords + 1], q[F::kWords];
-#pragma unroll
-          for (int m = 0; m <= F::kWords; ++m) raw[m] = pw[m];
-#pragma unroll
-          for (int m = 0; m < F::kWords; ++m) q[m] = __builtin_amdgcn_alignbyte(raw[m + 1], raw[m], sh);
+          // LDS reads at any byte alignment (gfx950 serves unaligned DS
+          // accesses); the payload needs no realignment in registers.
+          uint32_t sbits = 0, q[F::kWords];
+          __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
+          __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
           float u[32];
           F::decode(q, u);
           float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -332,16 +339,14 @@ gemv_kernel(const GemvArgs a) {
           s = b < slice_n ? blk_acc : s;
         }
         acc[i] = wave_sum63(s);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
     if (WT == 1) {
       if (lane == 63) {
 #pragma unroll
         for (int i = 0; i < R; ++i)
-          if (i < nrows) W.y[r0 + i - W.row_start] = acc[i];
+          if (i < nrows) cur.y[cur.r0 + i - cur.row_start] = acc[i];
       }
     } else {
       if (lane == 63) {
@@ -353,15 +358,13 @@ gemv_kernel(const GemvArgs a) {
         float s = red[parity][0][threadIdx.x];
 #pragma unroll
         for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
-        W.y[r0 + threadIdx.x - W.row_start] = s;
+        cur.y[cur.r0 + threadIdx.x - cur.row_start] = s;
       }
       parity ^= 1;
     }
     if (!more) break;
-    t = nt;
-    w = nw;
-    r0 = n0;
-    r1 = n1;
+    ++t;
+    cur = nxt;
   }
 }
 
@@ -398,19 +401,51 @@ __global__ void silu_mul_kernel(const float *g, const float *u, float *h, int64_
 }
 
 constexpr int kCarryThreads = 1024;
+constexpr int kCarryUnroll = 32;  // vectors up to 32768 floats take one load round trip
 
+__device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f)); }
+
+// One workgroup: every element is loaded once into registers (all loads issued
+// before any is used), the sum of squares is reduced in a fixed order (thread
+// partials by DPP per wave, then the 16 wave sums in order), then scaled.
 __global__ void __launch_bounds__(kCarryThreads)
 rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
   __shared__ float part[kCarryThreads / 64];
   const int tid = threadIdx.x;
   float ss = 0.0f;
+  if (n <= (int64_t)kCarryThreads * kCarryUnroll) {
+    float t[kCarryUnroll];
+#pragma unroll
+    for (int k = 0; k < kCarryUnroll; ++k) {
+      const int64_t i = tid + (int64_t)k * kCarryThreads;
+      t[k] = i < n ? v[i] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kCarryUnroll; ++k) {
+      if (gelu) t[k] = gelu_erf(t[k]);
+      ss = fmaf(t[k], t[k], ss);
+    }
+    ss = wave_sum63(ss);
+    if ((tid & 63) == 63) part[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCarryThreads / 64; ++i) tot += part[i];
+    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+#pragma unroll
+    for (int k = 0; k < kCarryUnroll; ++k) {
+      const int64_t i = tid + (int64_t)k * kCarryThreads;
+      if (i < n) out[i] = t[k] * inv;
+    }
+    return;
+  }
   for (int64_t i = tid; i < n; i += kCarryThreads) {
     float t = v[i];
-    if (gelu) t = 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
+    if (gelu) t = gelu_erf(t);
     ss = fmaf(t, t, ss);
   }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  ss = wave_sum63(ss);
+  if ((tid & 63) == 63) part[tid >> 6] = ss;
   __syncthreads();
   float tot = 0.0f;
 #pragma unroll
@@ -418,7 +453,7 @@ rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
   const float inv = 1.0f / sqrtf(tot / (float)n + eps);
   for (int64_t i = tid; i < n; i += kCarryThreads) {
     float t = v[i];
-    if (gelu) t = 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
+    if (gelu) t = gelu_erf(t);
     out[i] = t * inv;
   }
 }
