@@ -38,6 +38,28 @@ HBM_PEAK_GBS = 8000.0
 TOL = 1e-4
 
 
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the kernel source as it is now; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_q8_0_dense20b_44L_hbm_traffic.md")
+    src = os.path.join(ROOT, "quantized_gemv_gguf_amd", "csrc", "qgemv.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if "=" in line and not line.startswith(("#", "|", "`")):
+            k, v = [t.strip() for t in line.split("=", 1)]
+            vals[k] = v
+    if vals.get("kernel_source_sha256") != sha:
+        return None
+    v = vals.get(f"traffic_bytes_per_launch {kernel}")
+    return float(v) if v else None
+
+
 def threads() -> int:
     return int(os.environ.get("OMP_NUM_THREADS", 0) or min(16, os.cpu_count() or 1))
 
@@ -188,7 +210,8 @@ def dense_workload(args, dev):
                    "weight_bytes_per_token": model.bytes_per_token},
         "roofline": {"bound": "hbm", "kernel": f"gemv_q8_0_k{dom_k}", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_us": ms / cnt * 1e3, "bytes_per_launch": b / cnt},
+                     "traffic": profiled_traffic(f"gemv_q8_0_k{dom_k}"), "avg_launch_us": ms / cnt * 1e3,
+                     "bytes_per_launch": b / cnt},
         "kernels": kernels,
     }
     # identity: tokens/s = bandwidth / active bytes per token
@@ -239,35 +262,41 @@ def dense_parity(model, layers, n_rows=48, seed=7):
 
 
 def dense_cpu_baseline(model, seconds):
-    """The oracle (fp64, all threads) on the same pass, layer by layer from
-    token 0's carry, until `seconds` of oracle time have run."""
+    """The oracle (fp64, all threads) on the same pass: token after token,
+    layer by layer from token 0's carry, until `seconds` of oracle time have
+    run (weight regeneration for the oracle is not timed)."""
     import oracle
     t_oracle = 0.0
     nbytes = 0
     nth = threads()
     c = oracle.rms_carry(synth.x_vec(model.H, synth.seed_of(5, 999)).astype(np.float64), model.eps)
-    done = 0
-    for l in range(model.L):
-        ws = [synth.blocks(synth.Q8_0, r, k, model.seed(l, m), threads=nth) for m, (_, r, k) in enumerate(model.shapes)]
-        t = time.perf_counter()
-        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
-        c = oracle.rms_carry(y[2 * model.H:3 * model.H], model.eps)
-        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[1], *model.shapes[1][1:], c.astype(np.float32), threads=nth)
-        c = oracle.rms_carry(y, model.eps)
-        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[2], *model.shapes[2][1:], c.astype(np.float32), threads=nth)
-        act = oracle.rms_carry(y, model.eps, gelu=True)
-        y, _ = oracle.gemv_rows(oracle.Q8_0, ws[3], *model.shapes[3][1:], act.astype(np.float32), threads=nth)
-        c = oracle.rms_carry(y, model.eps)
-        t_oracle += time.perf_counter() - t
-        nbytes += sum(w.nbytes for w in ws)
-        done += 1
-        if t_oracle >= seconds:
-            break
+    layers_done = 0
+    tok = 0
+    while t_oracle < seconds:
+        for l in range(model.L):
+            ws = [synth.blocks(synth.Q8_0, r, k, model.seed(l, m), threads=nth)
+                  for m, (_, r, k) in enumerate(model.shapes)]
+            t = time.perf_counter()
+            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
+            c = oracle.rms_carry(y[2 * model.H:3 * model.H], model.eps)
+            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[1], *model.shapes[1][1:], c.astype(np.float32), threads=nth)
+            c = oracle.rms_carry(y, model.eps)
+            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[2], *model.shapes[2][1:], c.astype(np.float32), threads=nth)
+            act = oracle.rms_carry(y, model.eps, gelu=True)
+            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[3], *model.shapes[3][1:], act.astype(np.float32), threads=nth)
+            c = oracle.rms_carry(y, model.eps)
+            t_oracle += time.perf_counter() - t
+            nbytes += sum(w.nbytes for w in ws)
+            layers_done += 1
+            if t_oracle >= seconds:
+                break
+        tok += 1
     gbs = nbytes / t_oracle / 1e9
     return {"value": gbs, "unit": "GB/s", "cores": nth, "kind": "oracle",
             "tokens_per_s_equiv": gbs * 1e9 / model.bytes_per_token,
-            "sample": f"token 0, layers 0..{done - 1} of {model.L} ({4 * done} GEMVs, {nbytes / 1e9:.2f} GB), "
-                      f"fp64 scalar C oracle, {nth} threads, {t_oracle:.1f} s",
+            "sample": f"{layers_done} layer passes ({4 * layers_done} GEMVs, {nbytes / 1e9:.2f} GB of Q8_0 "
+                      f"weights, {tok} token(s) of the same 44-layer pass), fp64 scalar C oracle, "
+                      f"{nth} threads, {t_oracle:.1f} s",
             "cpu": cpu_model()}
 
 
