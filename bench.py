@@ -300,7 +300,229 @@ def dense_cpu_baseline(model, seconds):
             "cpu": cpu_model()}
 
 
-WORKLOADS = {"dense20b": dense_workload}
+
+# --- other workloads -------------------------------------------------------------------
+
+def _timed(fn, n, torch):
+    """(wall seconds, gpu ms) of n calls of fn() on the current stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1)
+
+
+def q4_0_workload(args, dev):
+    """Q4_0 4096x4096.  A single 9.4 MB matrix sits in the 256 MB MALL when
+    re-run, so the timed launches rotate over 128 distinct copies (1.21 GB);
+    also timed: one grid over 16 distinct matrices (151 MB) per launch, and
+    block_rows 0 vs 512 (bit-identical outputs)."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    c = synth.CONFIGS[2]
+    rows, k = c["rows"], c["k"]
+    nbytes = q.qgemv_weight_bytes(q.Q4_0, rows, k)
+    ncopy = 128
+    base = synth.blocks(q.Q4_0, rows, k, synth.seed_of(2, 0))
+    mats = [torch.from_numpy(base).to(dev) for _ in range(ncopy)]
+    x = torch.from_numpy(synth.x_vec(k, synth.seed_of(2, 9))).to(dev)
+    ys = torch.empty((16, rows), dtype=torch.float32, device=dev)
+    L = q.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    cm = [q.qg_matrix(m.data_ptr(), q.Q4_0, 0, rows, k, nbytes) for m in mats]
+
+    def one(i, B=0):
+        rc = L.qgemv_rows(ctypes.byref(cm[i % ncopy]), 0, rows, x.data_ptr(), ys[0].data_ptr(), B, st)
+        assert rc == 0
+
+    wins = [q.Window(q.Matrix(mats[j], q.Q4_0, rows, k), 0, rows, x, ys[j]) for j in range(16)]
+    arrs = []
+    for g in range(ncopy // 16):
+        ws = [q.Window(q.Matrix(mats[16 * g + j], q.Q4_0, rows, k), 0, rows, x, ys[j]) for j in range(16)]
+        arrs.append((q.qg_window * 16)(*[w.c() for w in ws]))
+
+    def grid(i):
+        rc = L.qgemv_windows(q.Q4_0, k, arrs[i % len(arrs)], 16, 0, st)
+        assert rc == 0
+
+    for i in range(max(args.warmup, 2)):
+        one(i)
+        grid(i)
+    n = max(args.steps, 64)
+    wall1, ms1 = _timed(one, n, torch)
+    wall16, ms16 = _timed(grid, n, torch)
+    y0 = torch.empty(rows, device=dev)
+    y512 = torch.empty(rows, device=dev)
+    L.qgemv_rows(ctypes.byref(cm[0]), 0, rows, x.data_ptr(), y0.data_ptr(), 0, st)
+    L.qgemv_rows(ctypes.byref(cm[0]), 0, rows, x.data_ptr(), y512.data_ptr(), 512, st)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y0.view(torch.int32), y512.view(torch.int32)))
+    res = {
+        "value": nbytes * 16 * n / (ms16 / 1e3) / 1e9,
+        "ms_per_step": ms16 / n,
+        "config": {"workload": c["name"], "format": "Q4_0", "rows": rows, "k": k,
+                   "launch": "one grid over 16 distinct matrices (151 MB), rotated over 128 copies"},
+        "single_matrix": {"us_per_launch": ms1 / n * 1e3, "GBs": nbytes * n / (ms1 / 1e3) / 1e9,
+                          "note": "one 9.4 MB matrix per launch, rotated over 128 copies"},
+        "block_rows_0_vs_512_bit_identical": same,
+    }
+    if not args.no_check:
+        import oracle
+        ref, a = oracle.gemv_rows(oracle.Q4_0, base, rows, k, x.cpu().numpy())
+        err = np.abs(y0.cpu().numpy().astype(np.float64) - ref)
+        res["parity"] = {"max_componentwise": float(np.max(err / a)),
+                         "max_normwise": float(err.max() / np.abs(ref).max()), "tol": TOL,
+                         "pass": bool(np.all(err <= TOL * a) and err.max() <= TOL * np.abs(ref).max())}
+    return res
+
+
+def moe_workload(args, dev):
+    """MXFP4 MoE expert GEMV: stacked (128, 2880, 2880) gate/up/down, 4 of 128
+    experts per token (seeded uniform top-4), 64 tokens.  Per token: one grid
+    over the 8 gate/up windows of the selected experts, SiLU*up, one grid over
+    the 4 down windows."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    c = synth.CONFIGS[4]
+    E, out, k, ns = c["n_expert"], c["out"], c["k"], c["n_sel"]
+    rows = E * out
+    host = [synth.blocks(q.MXFP4, rows, k, synth.seed_of(4, t)) for t in range(3)]
+    mats = [q.Matrix(torch.from_numpy(h).to(dev), q.MXFP4, rows, k) for h in host]
+    ids = synth.expert_ids(E, ns, c["tokens"], synth.seed_of(4, 8))
+    xs = torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(4, 100 + t)) for t in range(c["tokens"])])).to(dev)
+    gu = torch.empty(2 * ns * out, dtype=torch.float32, device=dev)
+    h = torch.empty(ns * out, dtype=torch.float32, device=dev)
+    y = torch.empty((c["tokens"], ns * out), dtype=torch.float32, device=dev)
+    L = q.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    m2 = (q.qg_matrix * 2)(mats[0].c(), mats[1].c())
+    m1 = (q.qg_matrix * 1)(mats[2].c())
+    idarr = [(ctypes.c_int32 * ns)(*[int(v) for v in ids[t]]) for t in range(c["tokens"])]
+    B = args.block_rows
+
+    def token(t):
+        t = t % c["tokens"]
+        rc = L.qgemv_expert_windows(m2, 2, E, idarr[t], ns, xs[t].data_ptr(), 0, gu.data_ptr(), B, st)
+        rc |= L.qgemv_silu_mul(gu.data_ptr(), gu.data_ptr() + 4 * ns * out, h.data_ptr(), ns * out, st)
+        rc |= L.qgemv_expert_windows(m1, 1, E, idarr[t], ns, h.data_ptr(), out, y[t].data_ptr(), B, st)
+        assert rc == 0
+
+    for t in range(args.warmup):
+        token(t)
+    n = args.steps if args.steps > 0 else c["tokens"]
+    wall, ms = _timed(token, n, torch)
+    per_tok = 3 * ns * q.qgemv_weight_bytes(q.MXFP4, out, k)
+    gbs = per_tok * n / wall / 1e9
+    return {"value": gbs, "ms_per_step": wall / n * 1e3, "tokens_per_s": n / wall,
+            "bytes_per_token": per_tok,
+            "config": {"workload": c["name"], "format": "MXFP4", "n_expert": E, "out": out, "k": k,
+                       "experts_per_token": ns, "tokens": n, "block_rows": B,
+                       "resident_bytes": 3 * q.qgemv_weight_bytes(q.MXFP4, rows, k)}}
+
+
+def ffn_streamed_workload(args, dev):
+    """Q8_0 FFN trio (gate/up 11008x4096, down 4096x11008) streamed from pinned
+    host memory through a lookahead-2 ring at block_rows 128/512/2048; the
+    host link is measured in the same run with one 256 MiB pinned H2D copy and
+    with copies of each block size.  Outputs are compared bit for bit with the
+    resident run."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    c = synth.CONFIGS[3]
+    H, F = c["hidden"], c["ffn"]
+    gate = synth.blocks(q.Q8_0, F, H, synth.seed_of(3, 0))
+    up = synth.blocks(q.Q8_0, F, H, synth.seed_of(3, 1))
+    down = synth.blocks(q.Q8_0, H, F, synth.seed_of(3, 2))
+
+    def pinned(a):
+        t = torch.empty(a.shape, dtype=torch.uint8, pin_memory=True)
+        t.numpy()[...] = a
+        return t
+
+    pin = [pinned(a) for a in (gate, up, down)]
+    res_w = [torch.from_numpy(a).to(dev) for a in (gate, up, down)]
+    x = torch.from_numpy(synth.x_vec(H, synth.seed_of(3, 9))).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g, u, hh, y = torch.empty(F, **f32), torch.empty(F, **f32), torch.empty(F, **f32), torch.empty(H, **f32)
+    per_tok = sum(a.nbytes for a in (gate, up, down))
+
+    def run(ws, streamer=None, B=0):
+        W = [q.Matrix(ws[0], q.Q8_0, F, H), q.Matrix(ws[1], q.Q8_0, F, H), q.Matrix(ws[2], q.Q8_0, H, F)]
+        if streamer is None:
+            q.qgemv_windows([q.Window(W[0], 0, F, x, g), q.Window(W[1], 0, F, x, u)])
+            q.qgemv_silu_mul(g, u, hh)
+            q.qgemv_rows(W[2], 0, H, hh, y)
+        else:
+            streamer.windows([q.Window(W[0], 0, F, x, g), q.Window(W[1], 0, F, x, u)], B)
+            q.qgemv_silu_mul(g, u, hh)
+            streamer.rows(W[2], 0, H, hh, y, B)
+
+    run(res_w)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    # host link: one 256 MiB pinned copy, and copies of each block size
+    big = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dbig = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dbig.copy_(big, non_blocking=True)
+    wall, ms = _timed(lambda i: dbig.copy_(big, non_blocking=True), 5, torch)
+    link_256 = (256 << 20) * 5 / (ms / 1e3) / 1e9
+    out = {}
+    rb_down = q.qgemv_weight_bytes(q.Q8_0, 1, F)
+    for B in (128, 512, 2048):
+        blk = B * rb_down
+        wall_c, ms_c = _timed(lambda i: dbig[:blk].copy_(big[:blk], non_blocking=True), 64, torch)
+        with q.Streamer(B * rb_down, c["lookahead"]) as stv:
+            for _ in range(max(args.warmup, 1)):
+                run(pin, stv, B)
+            torch.cuda.synchronize()
+            n = max(args.steps, 8)
+            wall_s, ms_s = _timed(lambda i: run(pin, stv, B), n, torch)
+            same = bool(torch.equal(y.view(torch.int32), ref.view(torch.int32)))
+            link = per_tok * n / wall_s / 1e9
+            out[str(B)] = {"link_GBs": link, "ms_per_token": wall_s / n * 1e3,
+                           "pct_of_256MiB_copy": 100 * link / link_256,
+                           "copy_GBs_at_block_size": blk * 64 / (ms_c / 1e3) / 1e9,
+                           "bit_identical_to_resident": same, "ring_bytes": stv.ring_bytes}
+    best = max(out, key=lambda b: out[b]["link_GBs"])
+    return {"value": out[best]["link_GBs"], "ms_per_step": out[best]["ms_per_token"], "unit_note":
+            "host-link GB/s of the streamed pass (weight bytes copied / wall time)",
+            "bytes_per_token": per_tok, "h2d_256MiB_GBs": link_256, "block_rows": out,
+            "config": {"workload": c["name"], "format": "Q8_0", "hidden": H, "ffn": F,
+                       "lookahead": c["lookahead"], "best_block_rows": int(best)}}
+
+
+def q8_0_small_workload(args, dev):
+    """Q8_0 256x1024: a launch-latency case (278 KB of weights)."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    c = synth.CONFIGS[1]
+    rows, k = c["rows"], c["k"]
+    w = torch.from_numpy(synth.blocks(q.Q8_0, rows, k, synth.seed_of(1, 0))).to(dev)
+    x = torch.from_numpy(synth.x_vec(k, synth.seed_of(1, 9))).to(dev)
+    y = torch.empty(rows, device=dev)
+    L = q.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    m = q.Matrix(w, q.Q8_0, rows, k).c()
+
+    def one(i):
+        assert L.qgemv_rows(ctypes.byref(m), 0, rows, x.data_ptr(), y.data_ptr(), 0, st) == 0
+
+    for i in range(10):
+        one(i)
+    n = max(args.steps, 200)
+    wall, ms = _timed(one, n, torch)
+    nbytes = w.numel()
+    return {"value": nbytes * n / (ms / 1e3) / 1e9, "ms_per_step": ms / n,
+            "config": {"workload": c["name"], "format": "Q8_0", "rows": rows, "k": k,
+                       "note": "weights stay in cache across launches; a latency figure, not an HBM one"}}
+
+WORKLOADS = {"dense20b": dense_workload, "q4_0_4096": q4_0_workload, "moe_mxfp4": moe_workload,
+             "ffn_streamed": ffn_streamed_workload, "q8_0_256": q8_0_small_workload}
 
 
 # --- entry --------------------------------------------------------------------------
@@ -316,6 +538,7 @@ def main(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--block-rows", type=int, default=0, help="block_rows for the MoE workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a 256 MiB device-to-device copy (a kernel of known traffic, to scale HBM counters)")
     args = p.parse_args(argv)
