@@ -223,11 +223,13 @@ void orc_silu_mul(const double *g, const double *u, double *h, int64_t n) {
 
 /* Carry step of the synthetic dense decode pass: optional exact GELU
  * (0.5 v (1 + erf(v / sqrt 2)), GPT-NeoX's activation), then RMS
- * normalisation v / sqrt(mean(v^2) + eps) with no gain. */
+ * normalisation v / sqrt(mean(v^2) + eps) with no gain.  The GELU is written
+ * with erfc, since 1 + erf(z) = erfc(-z) exactly: erfc keeps its relative
+ * accuracy for v far below 0, where 1 + erf cancels to nothing. */
 void orc_rms_carry(const double *v, double *out, int64_t n, double eps, int32_t gelu) {
   double ss = 0.0;
   for (int64_t i = 0; i < n; ++i) {
-    double t = gelu ? 0.5 * v[i] * (1.0 + erf(v[i] / sqrt(2.0))) : v[i];
+    double t = gelu ? 0.5 * v[i] * erfc(-v[i] / sqrt(2.0)) : v[i];
     out[i] = t;
     ss += t * t;
   }

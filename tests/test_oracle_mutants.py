@@ -40,7 +40,8 @@ MUTANTS = [
     ("abs_sum_signed", "aacc += fabs(p);", "aacc += p;"),
     ("silu_sign", "h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];", "h[i] = g[i] / (1.0 + exp(g[i])) * u[i];"),
     ("rms_mean_dropped", "1.0 / sqrt(ss / (double)n + eps)", "1.0 / sqrt(ss + eps)"),
-    ("gelu_scale", "erf(v[i] / sqrt(2.0))", "erf(v[i])"),
+    ("gelu_scale", "erfc(-v[i] / sqrt(2.0))", "erfc(-v[i])"),
+    ("gelu_cancelling", "0.5 * v[i] * erfc(-v[i] / sqrt(2.0))", "0.5 * v[i] * (1.0 + erf(v[i] / sqrt(2.0)))"),
 ]
 
 # pins, cheapest first; a mutant is caught at the first one that fails

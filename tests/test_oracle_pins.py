@@ -342,3 +342,9 @@ def test_rms_carry_closed_forms():
     g = oracle.rms_carry(v, eps=0.0, gelu=True)
     t = v * norm.cdf(v)
     assert np.allclose(g, t / np.sqrt(np.mean(t ** 2)), rtol=1e-12, atol=1e-14)
+    # ... to full relative accuracy far below 0, where every GELU value is tiny
+    # and the normalisation scales them back up to O(1)
+    v = -np.linspace(5.0, 30.0, 51)
+    g = oracle.rms_carry(v, eps=0.0, gelu=True)
+    t = v * norm.cdf(v)
+    assert np.allclose(g, t / np.sqrt(np.mean(t ** 2)), rtol=1e-10, atol=0)
