@@ -129,6 +129,43 @@ class DensePass:
     def seed(layer, m):
         return synth.seed_of(5, 4 * layer + m)
 
+    # -- the pass as one chain: one persistent launch per token --
+    def build_chain(self):
+        """Steps (l, m) in pass order, each with its own output buffer; the
+        carry is fused into the next step's x-load.  The last step writes
+        `xin`, which the first step of the next token normalises."""
+        torch, q = self.torch, self.q
+        H, F = self.H, self.F
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        self.xin = self.x0.clone()
+        self.ys = []
+        steps = []
+        prev = self.xin
+        for l in range(self.L):
+            outs = [torch.empty(3 * H, **f32), torch.empty(H, **f32), torch.empty(F, **f32),
+                    self.xin if l == self.L - 1 else torch.empty(H, **f32)]
+            srcs = [prev, outs[0][2 * H:3 * H], outs[1], outs[2]]
+            ops = [q.IN_RMS, q.IN_RMS, q.IN_RMS, q.IN_GELU_RMS]
+            for m, (_, r, k) in enumerate(self.shapes):
+                W = q.Matrix(self.w[l][m], q.Q8_0, r, k)
+                steps.append(q.ChainStep([q.ChainWindow(W, 0, r, srcs[m], outs[m])], ops[m], self.eps))
+            self.ys.append((outs, srcs, ops))
+            prev = outs[3]
+        self.chain = q.Chain(q.Q8_0, steps)
+        self.chain_handle = ctypes.c_void_p(self.chain.handle)
+
+    def reset_chain(self):
+        self.xin.copy_(self.x0)
+
+    def token_chain(self, ev=None):
+        if ev is not None:
+            ev[0].record()
+        rc = self.lib.qgemv_chain_run(self.chain_handle, self.stream)
+        if ev is not None:
+            ev[1].record()
+        if rc != 0:
+            raise RuntimeError(f"qgemv_chain_run failed: {rc}")
+
     def reset(self):
         """c = rms(x0): the carry the first token starts from."""
         rc = self.lib.qgemv_rms_carry(self.x0.data_ptr(), self.c.data_ptr(), self.H, self.eps, 0, self.stream)
@@ -162,6 +199,8 @@ def dense_workload(args, dev):
     c = synth.CONFIGS[5]
     layers = args.layers or c["layers"]
     model = DensePass(layers, c["hidden"], c["ffn"], dev)
+    if not args.separate:
+        return dense_chain_workload(args, dev, model, c, layers)
     torch.cuda.synchronize()
     model.reset()
     for _ in range(args.warmup):
@@ -221,6 +260,90 @@ def dense_workload(args, dev):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = dense_cpu_baseline(model, args.cpu_seconds)
     return res
+
+
+def dense_chain_workload(args, dev, model, c, layers):
+    """The pass as one chain launch per token (qgemv_chain_run)."""
+    import torch
+    model.build_chain()
+    model.reset_chain()
+    for _ in range(args.warmup):
+        model.token_chain()
+    model.chain.check()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    for s in range(args.steps):
+        model.token_chain(events[s])
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    model.chain.check()
+    gpu_ms = g0.elapsed_time(g1)
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    b = model.bytes_per_token
+    gbs = b * args.steps / wall / 1e9
+    achieved = b / (avg_ms / 1e3) / 1e9
+    kname = "chain_q8_0_dense20b"
+    res = {
+        "value": gbs,
+        "ms_per_step": wall / args.steps * 1e3,
+        "tokens_per_s": args.steps / wall,
+        "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "gpu_event_ms_per_step": gpu_ms / args.steps,
+        "bytes_per_token": b,
+        "config": {"workload": c["name"], "layers": layers, "hidden": c["hidden"], "ffn": c["ffn"],
+                   "format": "Q8_0", "tokens": args.steps, "gemvs_per_token": len(model.calls),
+                   "weight_bytes_per_token": b, "launch": "one chain launch per token",
+                   "grid_workgroups": model.chain.grid},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(kname),
+                     "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": b},
+        "kernels": {kname: {"launches": args.steps, "avg_us": avg_ms * 1e3, "min_us": min(launch_ms) * 1e3,
+                            "max_us": max(launch_ms) * 1e3, "avg_bytes": b, "GBs": achieved}},
+    }
+    assert abs(res["tokens_per_s"] - gbs * 1e9 / b) <= 1e-9 * res["tokens_per_s"]
+    if not args.no_check:
+        res["parity"] = dense_chain_parity(model, layers)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = dense_cpu_baseline(model, args.cpu_seconds)
+    return res
+
+
+def dense_chain_parity(model, layers, n_rows=48, seed=7):
+    """Teacher-forced check of one more chain token: for every step of layers
+    0 and layers-1, the oracle normalises the GPU's own input vector in fp64
+    and multiplies sampled rows (weights regenerated on the host)."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(seed)
+    x_first = model.xin.clone()
+    model.token_chain()
+    model.chain.check()
+    torch.cuda.synchronize()
+    worst_n, worst_c, checked = 0.0, 0.0, 0
+    for l in sorted({0, layers - 1}):
+        outs, srcs, ops = model.ys[l]
+        for m, (_, r, k) in enumerate(model.shapes):
+            src = x_first if (l == 0 and m == 0) else srcs[m]
+            x = oracle.rms_carry(src.cpu().numpy().astype(np.float64), model.eps, gelu=(m == 3))
+            y = outs[m].cpu().numpy().astype(np.float64)
+            rows = np.sort(rng.choice(r, n_rows, replace=False))
+            ref, a = np.empty(n_rows), np.empty(n_rows)
+            for j, row in enumerate(rows):
+                wrow = synth.blocks(synth.Q8_0, r, k, model.seed(l, m), r0=int(row), r1=int(row) + 1, threads=1)
+                ref[j], a[j] = [v[0] for v in oracle.gemv_rows(oracle.Q8_0, wrow, 1, k, x, threads=1)]
+            err = np.abs(y[rows] - ref)
+            worst_c = max(worst_c, float(np.max(err / a)))
+            worst_n = max(worst_n, float(err.max() / np.abs(ref).max()))
+            checked += n_rows
+    ok = worst_c <= TOL and worst_n <= TOL
+    return {"rows_checked": checked, "max_componentwise": worst_c, "max_normwise_sampled": worst_n,
+            "tol": TOL, "pass": bool(ok), "teacher_forced": "fp64 rms of the GPU's own step inputs"}
 
 
 def dense_parity(model, layers, n_rows=48, seed=7):
@@ -535,6 +658,8 @@ def main(argv=None):
     p.add_argument("--workload", default="dense20b",
                    choices=sorted(WORKLOADS))
     p.add_argument("--layers", type=int, default=0, help="fewer layers for a quick run (not a valid headline)")
+    p.add_argument("--separate", action="store_true",
+                   help="dense pass as separate launches (GEMV, then carry) instead of one chain per token")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -72,15 +72,19 @@ enum qg_status {
                            weight data not 16-byte aligned */
   QG_E_NOT_PINNED = -7, /* streamed weights not in page-locked host memory */
   QG_E_CAPACITY = -8,   /* a streamed row block is larger than a ring slot */
+  QG_E_BARRIER = -9,    /* a chain's device-wide barrier gave up waiting */
   QG_E_HIP = -100       /* a HIP runtime call failed; see qgemv_last_hip_error */
 };
 
 /* Most windows one grid takes (the window table travels in kernel arguments). */
 #define QG_MAX_WINDOWS 64
 
-/* Largest k: a row's block columns are spread over at most 8 wavefronts with
- * at most 3 columns per lane, each lane holding its activations in registers. */
+/* Largest k: a row's block columns are spread over at most 12 wavefronts with
+ * at most 2 columns per lane, each lane holding its activations in registers. */
 #define QG_MAX_K 49152
+
+/* Largest k of a chain step: 12 wavefronts, one column per lane. */
+#define QG_CHAIN_MAX_K 24576
 
 /* A whole quantized weight matrix: the compact resident representation of a
  * quantized tensor (RAMforge README, "Milestone 5", QuantizedTensor: raw block
@@ -195,6 +199,72 @@ int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_windo
 
 /* Waits for the streamer's work, frees it.  NULL is a no-op. */
 int qgemv_stream_destroy(qg_streamer *st);
+
+/* ---- chains: dependent GEMVs in one persistent grid ----
+ * A decode pass is a sequence of GEMVs, each taking the previous one's output
+ * through a small transform.  Launched one by one, every GEMV ends with a
+ * drain: the last rows finish while HBM idles, and the next launch ramps up
+ * from nothing.  A chain runs the whole sequence as ONE launch that spans it
+ * (neurostream README, "What the numbers taught us": one pipeline per
+ * projection drained once per projection; a plan spanning the layer removed
+ * those drains).  Workgroups stay resident, wait at a device-wide barrier
+ * between steps, and fetch the weights of their next step before waiting,
+ * since weights do not depend on the input.
+ *
+ * Step s computes, for each of its windows, y = W[row_start:row_end] . op(x),
+ * with op applied as the kernel loads x:
+ *   QG_IN_X         x
+ *   QG_IN_RMS       rms(x), as qgemv_rms_carry(gelu = 0)
+ *   QG_IN_GELU_RMS  rms(gelu(x)), as qgemv_rms_carry(gelu = 1)
+ *   QG_IN_SILU_MUL  silu(x) * x2, as qgemv_silu_mul
+ * Steps run in order and see everything earlier steps wrote.  Each row is
+ * computed in qgemv_rows' per-row order and each transform in the order of
+ * the call named beside it, so a chain gives the same bits as the equivalent
+ * sequence of separate calls. */
+enum qg_in_op { QG_IN_X = 0, QG_IN_RMS = 1, QG_IN_GELU_RMS = 2, QG_IN_SILU_MUL = 3 };
+
+typedef struct qg_chain_window {
+  const void *data;  /* the matrix's row 0, device, 16-byte aligned */
+  int64_t n_rows;    /* rows of that matrix, for range checks */
+  int64_t row_start; /* first row of the window */
+  int64_t row_end;   /* one past the last row */
+  const float *x;    /* device, k values: the transform's input */
+  const float *x2;   /* device, k values: the multiplier of QG_IN_SILU_MUL, else unused */
+  float *y;          /* device, row_end - row_start values */
+} qg_chain_window;
+
+typedef struct qg_chain_step {
+  int64_t k;         /* inputs per row: a multiple of 32, at most QG_CHAIN_MAX_K */
+  int32_t first_win; /* the step's windows: win[first_win .. first_win + n_win) */
+  int32_t n_win;     /* >= 1 (windows may be empty) */
+  int32_t in_op;     /* enum qg_in_op; the RMS ops need one x shared by all windows */
+  float eps;         /* >= 0, for the RMS ops */
+} qg_chain_step;
+
+typedef struct qg_chain qg_chain;
+
+/* Validates and uploads a chain of n_steps steps over the host arrays steps
+ * and win (all windows of one fmt), sized for the current device.  The chain
+ * keeps the pointers, not the data: every buffer must outlive its runs.
+ * Within a step, a window's y must not overlap any x, x2 or other y of that
+ * step, and no step may write weights.  Synchronising. */
+int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
+                       const qg_chain_window *win, int32_t n_win, qg_chain **out);
+
+/* Enqueues one run of every step on `stream` (one cooperative launch on the
+ * chain's device, which must be current).  Runs of one chain must not overlap:
+ * they share its barrier state. */
+int qgemv_chain_run(qg_chain *c, qg_stream_t stream);
+
+/* Waits for the device, then QG_OK, or QG_E_BARRIER if a run's barrier gave
+ * up (its outputs are then undefined; the state is reset for the next run). */
+int qgemv_chain_check(qg_chain *c);
+
+/* Workgroups a run launches (one per compute unit), or a negative status. */
+int64_t qgemv_chain_grid(const qg_chain *c);
+
+/* Waits for the device, frees the chain.  NULL is a no-op. */
+int qgemv_chain_destroy(qg_chain *c);
 
 /* Static text for a status. */
 const char *qgemv_strerror(int status);

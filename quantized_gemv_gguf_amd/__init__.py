@@ -18,11 +18,13 @@ Q8_0, Q4_0, MXFP4 = 1, 2, 3
 FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "mxfp4": MXFP4}
 MAX_WINDOWS = 64
 MAX_K = 49152
+CHAIN_MAX_K = 24576
+IN_X, IN_RMS, IN_GELU_RMS, IN_SILU_MUL = 0, 1, 2, 3
 
 QG_OK = 0
 STATUS = {
     -1: "QG_E_NULL", -2: "QG_E_FMT", -3: "QG_E_SHAPE", -4: "QG_E_RANGE", -5: "QG_E_SIZE",
-    -6: "QG_E_ARG", -7: "QG_E_NOT_PINNED", -8: "QG_E_CAPACITY", -100: "QG_E_HIP",
+    -6: "QG_E_ARG", -7: "QG_E_NOT_PINNED", -8: "QG_E_CAPACITY", -9: "QG_E_BARRIER", -100: "QG_E_HIP",
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +51,15 @@ class qg_matrix(ctypes.Structure):
 class qg_window(ctypes.Structure):
     _fields_ = [("data", _vp), ("n_rows", _i64), ("row_start", _i64), ("row_end", _i64),
                 ("x", _vp), ("y", _vp)]
+
+
+class qg_chain_window(ctypes.Structure):
+    _fields_ = [("data", _vp), ("n_rows", _i64), ("row_start", _i64), ("row_end", _i64),
+                ("x", _vp), ("x2", _vp), ("y", _vp)]
+
+
+class qg_chain_step(ctypes.Structure):
+    _fields_ = [("k", _i64), ("first_win", _i32), ("n_win", _i32), ("in_op", _i32), ("eps", ctypes.c_float)]
 
 
 _lib = None
@@ -79,6 +90,11 @@ def lib():
         "qgemv_stream_rows": ([_vp, P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
         "qgemv_stream_windows": ([_vp, _i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_stream_destroy": ([_vp], ctypes.c_int),
+        "qgemv_chain_create": ([_i32, P(qg_chain_step), _i32, P(qg_chain_window), _i32, P(_vp)], ctypes.c_int),
+        "qgemv_chain_run": ([_vp, _vp], ctypes.c_int),
+        "qgemv_chain_check": ([_vp], ctypes.c_int),
+        "qgemv_chain_grid": ([_vp], _i64),
+        "qgemv_chain_destroy": ([_vp], ctypes.c_int),
         "qgemv_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "qgemv_last_hip_error": ([], ctypes.c_char_p),
         "qgemv_version": ([], ctypes.c_char_p),
@@ -270,6 +286,92 @@ class Streamer:
 
 def qgemv_stream_create(slot_bytes: int, lookahead: int) -> Streamer:
     return Streamer(slot_bytes, lookahead)
+
+
+@dataclass
+class ChainWindow:
+    """Rows [row_start, row_end) of ``mat``: y = W[row_start:row_end] . op(x),
+    op the step's input transform (``x2`` is the multiplier of IN_SILU_MUL)."""
+    mat: Matrix
+    row_start: int
+    row_end: int
+    x: object
+    y: object
+    x2: object = None
+
+
+@dataclass
+class ChainStep:
+    """One step of a chain: its windows (same fmt and k) and input transform."""
+    windows: Sequence[ChainWindow]
+    in_op: int = IN_X
+    eps: float = 1e-6
+
+
+def _chain_tables(steps: Sequence[ChainStep]):
+    wins, cs = [], []
+    for st in steps:
+        if not st.windows:
+            raise ValueError("a chain step needs at least one window")
+        k = st.windows[0].mat.k
+        first = len(wins)
+        for w in st.windows:
+            if w.mat.k != k:
+                raise ValueError("the windows of a chain step must share k")
+            n = max(w.row_end - w.row_start, 0)
+            x2 = _f32(w.x2, k, "x2") if w.x2 is not None else 0
+            wins.append(qg_chain_window(_ptr(w.mat.data), int(w.mat.n_rows), int(w.row_start), int(w.row_end),
+                                        _f32(w.x, k, "x"), x2, _f32(w.y, n, "y")))
+        cs.append(qg_chain_step(int(k), first, len(st.windows), int(st.in_op), float(st.eps)))
+    return (qg_chain_step * len(cs))(*cs), len(cs), (qg_chain_window * len(wins))(*wins), len(wins)
+
+
+class Chain:
+    """Owner of a qg_chain: the steps run in order by one launch per run()."""
+
+    def __init__(self, fmt: int, steps: Sequence[ChainStep]):
+        sarr, ns, warr, nw = _chain_tables(steps)
+        h = _vp()
+        _check(lib().qgemv_chain_create(int(fmt), sarr, ns, warr, nw, ctypes.byref(h)), "qgemv_chain_create")
+        self._h = h
+        self._keep = list(steps)  # the tensors must outlive the chain
+        self.fmt = int(fmt)
+        self.n_steps = ns
+
+    @property
+    def grid(self) -> int:
+        return int(lib().qgemv_chain_grid(self._h))
+
+    @property
+    def handle(self) -> int:
+        return int(self._h.value)
+
+    def run(self, stream=None) -> None:
+        _check(lib().qgemv_chain_run(self._h, _stream(stream)), "qgemv_chain_run")
+
+    def check(self) -> None:
+        _check(lib().qgemv_chain_check(self._h), "qgemv_chain_check")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            h, self._h = self._h, None
+            _check(lib().qgemv_chain_destroy(h), "qgemv_chain_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def qgemv_chain_create(fmt: int, steps: Sequence[ChainStep]) -> Chain:
+    return Chain(fmt, steps)
 
 
 def qgemv_version() -> str:

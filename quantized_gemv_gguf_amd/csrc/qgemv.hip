@@ -14,7 +14,7 @@
 //   t owns the block columns j = t + T*c (c < C) of every row it touches, and
 //   keeps the 32 activations of each such column in registers, loaded once per
 //   window.  A row is one pass: each lane dots its C blocks (32 weights each),
-//   the 64 lanes of a wave are combined by a fixed xor butterfly, and for
+//   the 64 lanes of a wave are combined by fixed DPP shifts, and for
 //   WT > 1 the per-wave sums go through LDS and are added in wave order.
 //   (WT, C) is a function of (format, k) only, and so is the whole per-row
 //   operation order: a row gives the same bits whichever window, row block,
@@ -175,11 +175,33 @@ __device__ __forceinline__ float wave_sum63(float v) {
   return v;
 }
 
-// Same sum, every lane holding it (xor butterfly); used off the hot path.
-__device__ __forceinline__ float wave_sum(float v) {
+// One wave's partial sum for one staged row: lane l dots blocks l + 64c
+// (c < C) of the wave's slice, staged at byte `ph` of `sb`, with its
+// registered activations.  Fixed order: four FMA chains per block combined
+// as (p0 + p1) + (p2 + p3), the block scale applied once, blocks in c order.
+template <int FMT, int C>
+__device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane, int slice_n,
+                                             const float (&xr)[C][32]) {
+  using F = Fmt<FMT>;
+  float s = 0.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  for (int c = 0; c < C; ++c) {
+    const int b = lane + 64 * c;
+    const int bo = ph + F::kBytes * b;  // block's byte offset in the staged row
+    // LDS reads at any byte alignment (gfx950 serves unaligned DS accesses):
+    // the payload needs no realignment in registers.
+    uint32_t sbits = 0, q[F::kWords];
+    __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
+    __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
+    float u[32];
+    F::decode(q, u);
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
+    const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
+    s = b < slice_n ? blk_acc : s;
+  }
+  return s;
 }
 
 // Largest rows per tile, per (format, block columns per lane): the fetched
@@ -320,24 +342,7 @@ gemv_kernel(const GemvArgs a) {
         // operations of one wave complete in order).
         __builtin_amdgcn_wave_barrier();
         const int ph = (int)((uintptr_t)(cur.base + slice_off + (cur.r0 + i) * rb) & 15);
-        float s = 0.0f;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int b = lane + 64 * c;
-          const int bo = ph + BB * b;  // block's byte offset in the staged row
-          // LDS reads at any byte alignment (gfx950 serves unaligned DS
-          // accesses); the payload needs no realignment in registers.
-          uint32_t sbits = 0, q[F::kWords];
-          __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
-          __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
-          float u[32];
-          F::decode(q, u);
-          float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
-          const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
-          s = b < slice_n ? blk_acc : s;
-        }
+        const float s = row_partial<FMT, C>(sb, ph, lane, slice_n, xr);
         acc[i] = wave_sum63(s);
         __builtin_amdgcn_wave_barrier();
       }
@@ -401,29 +406,41 @@ __global__ void silu_mul_kernel(const float *g, const float *u, float *h, int64_
 }
 
 constexpr int kCarryThreads = 1024;
-constexpr int kCarryUnroll = 32;  // vectors up to 32768 floats take one load round trip
 
-__device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f)); }
+// Exact (erf) GELU, evaluated as 0.5 t erfc(-t / sqrt 2): equal to
+// 0.5 t (1 + erf(t / sqrt 2)), without that form's cancellation for t far
+// below 0 (which an RMS normalisation of small GELU values would magnify).
+__device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * erfcf(-t * 0.70710678118654752f); }
 
-// One workgroup: every element is loaded once into registers (all loads issued
-// before any is used), the sum of squares is reduced in a fixed order (thread
-// partials by DPP per wave, then the 16 wave sums in order), then scaled.
+// One workgroup, 16 waves.  For n a multiple of 32 up to 32768 (every k a
+// GEMV takes in one pass), thread t owns elements [32t, 32t + 32): it loads
+// them once, sums their squares in element order, the lanes of a wave are
+// combined by wave_sum63 and the 16 wave sums added in wave order.  The chain
+// kernel forms the same sum in the same order from the same lanes, so both
+// give identical bits.  Other n: a strided loop, same reduction tree.
 __global__ void __launch_bounds__(kCarryThreads)
 rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
   __shared__ float part[kCarryThreads / 64];
   const int tid = threadIdx.x;
   float ss = 0.0f;
-  if (n <= (int64_t)kCarryThreads * kCarryUnroll) {
-    float t[kCarryUnroll];
+  if (n % 32 == 0 && n <= 32 * kCarryThreads) {
+    const int nb = (int)(n / 32);
+    const bool ok = tid < nb;
+    const float *p = v + 32 * min(tid, nb - 1);
+    float t[32];
 #pragma unroll
-    for (int k = 0; k < kCarryUnroll; ++k) {
-      const int64_t i = tid + (int64_t)k * kCarryThreads;
-      t[k] = i < n ? v[i] : 0.0f;
+    for (int q = 0; q < 8; ++q) {
+      float4 w;
+      __builtin_memcpy(&w, p + 4 * q, 16);
+      t[4 * q + 0] = ok ? w.x : 0.0f;
+      t[4 * q + 1] = ok ? w.y : 0.0f;
+      t[4 * q + 2] = ok ? w.z : 0.0f;
+      t[4 * q + 3] = ok ? w.w : 0.0f;
     }
 #pragma unroll
-    for (int k = 0; k < kCarryUnroll; ++k) {
-      if (gelu) t[k] = gelu_erf(t[k]);
-      ss = fmaf(t[k], t[k], ss);
+    for (int e = 0; e < 32; ++e) {
+      if (gelu) t[e] = gelu_erf(t[e]);
+      ss = fmaf(t[e], t[e], ss);
     }
     ss = wave_sum63(ss);
     if ((tid & 63) == 63) part[tid >> 6] = ss;
@@ -432,10 +449,13 @@ rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
 #pragma unroll
     for (int i = 0; i < kCarryThreads / 64; ++i) tot += part[i];
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+    if (ok) {
+      float *o = out + 32 * tid;
 #pragma unroll
-    for (int k = 0; k < kCarryUnroll; ++k) {
-      const int64_t i = tid + (int64_t)k * kCarryThreads;
-      if (i < n) out[i] = t[k] * inv;
+      for (int q = 0; q < 8; ++q) {
+        const float4 w = make_float4(t[4 * q] * inv, t[4 * q + 1] * inv, t[4 * q + 2] * inv, t[4 * q + 3] * inv);
+        __builtin_memcpy(o + 4 * q, &w, 16);
+      }
     }
     return;
   }
@@ -455,6 +475,388 @@ rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
     float t = v[i];
     if (gelu) t = gelu_erf(t);
     out[i] = t * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chain: dependent GEMV steps in one persistent grid
+// ---------------------------------------------------------------------------
+//
+// One workgroup of kChainWaves waves per CU stays resident for the whole
+// chain.  In each step a team is ceil(nb/64) of those waves (one block column
+// per lane, as in gemv_kernel with C = 1), a workgroup holds 12 / WT teams,
+// and team tau of the grid takes tiles tau, tau + T, tau + 2T, ...  Between
+// steps every workgroup waits at a device-wide barrier, because the next
+// step's input is the previous step's output.  Weights never depend on it:
+// during its last tile of a step a wave already fetches the rows of its next
+// tile, in whichever later step that is, so those loads are in flight while
+// the barrier completes (wave 0, which runs the barrier, fetches right after
+// arriving instead).  The input transform (RMS, GELU + RMS,
+// SiLU * up) is applied as x is loaded into registers; the sum of squares of
+// the RMS is formed in the order qgemv_rms_carry uses (32 consecutive
+// elements per lane, the lanes of a wave by wave_sum63, the waves in order),
+// so a chain reproduces the separate calls bit for bit.
+
+constexpr int kChainWaves = 12;
+constexpr unsigned kSpinLimit = 1u << 22;  // barrier polls before giving up (seconds)
+
+struct ChainWinDev {
+  const uint8_t *base;
+  const float *x, *x2;
+  float *y;
+  int64_t row_start, row_end;
+};
+
+struct ChainStepDev {
+  const float *xs;  // the RMS ops' shared x (first non-empty window's)
+  int64_t row_bytes;
+  int32_t win0, n_win, pre0;  // windows [win0, win0 + n_win); their tile prefix at pre0
+  int32_t in_op, nb, wt, tpw, tile_rows, n_tiles;
+  float eps;
+};
+
+// Barrier state, one 256-byte line per word.  `count` returns to 0 after every
+// barrier and `gen` only grows (wrapping): barrier b of a launch is complete
+// once gen reaches base + b, base being gen at the launch's start, which the
+// host tracks from run to run.
+struct ChainSync {
+  unsigned count, pad0[63];
+  unsigned gen, pad1[63];
+  unsigned fail, pad2[63];
+};
+
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained
+
+// Split-phase device-wide barrier, run by wave 0 of each workgroup as a whole
+// wave (every branch uniform).  Every release step below waits for all of
+// the wave's outstanding memory operations, so all of them happen before the
+// wave fetches the next step's weights: only the wait for the barrier itself
+// overlaps that fetch.
+//   arrive: release fence (L2 write-back of the workgroup's stores; the
+//     compiler's own wait after it can be dropped when nothing else is
+//     outstanding, so an explicit one follows), then add 1 to `count`.  The
+//     last arrival acquires, resets `count`, releases, and publishes `target`.
+//   wait: unless last, poll `gen` until it reaches `target`, then acquire.
+// A barrier still incomplete after kSpinLimit polls marks `fail` and lets the
+// workgroup through, so the kernel always ends; the host reports it.
+__device__ __forceinline__ bool chain_arrive(ChainSync *sy, unsigned n_groups, unsigned target, int wid) {
+  __syncthreads();
+  bool last = false;
+  if (wid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    const unsigned arrived = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_fetch_add(&sy->count, threadIdx.x == 0 ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    last = arrived == n_groups - 1;
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(&sy->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __hip_atomic_store(&sy->gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return last;
+}
+
+__device__ __forceinline__ void chain_wait(ChainSync *sy, unsigned target, bool last, int wid) {
+  if (wid == 0 && !last) {
+    for (unsigned spins = 1;; ++spins) {
+      const unsigned g =
+          __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sy->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if ((int)(g - target) >= 0) break;
+      if ((spins & 63) == 0) {
+        const unsigned f = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&sy->fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (f || spins >= kSpinLimit) {
+          __hip_atomic_store(&sy->fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Pointers read from the chain's device tables lose their address space; the
+// kernel marks them global so that loads and stores are global_* (flat ones
+// would also count against the LDS counter and stall every LDS wait on the
+// weight prefetch).
+#define QG_GLOBAL __attribute__((address_space(1)))
+// The step, window and tile tables never change during a launch: read through
+// the constant address space they become scalar loads, which neither wait on
+// nor hold up the vector loads of the weights (as plain global loads after the
+// barrier's fences they would be vector loads, each draining the prefetch).
+#define QG_CONST __attribute__((address_space(4)))
+
+__device__ __forceinline__ ChainStepDev load_step(const QG_CONST ChainStepDev *p) {
+  ChainStepDev d;
+  d.xs = p->xs;
+  d.row_bytes = p->row_bytes;
+  d.win0 = p->win0;
+  d.n_win = p->n_win;
+  d.pre0 = p->pre0;
+  d.in_op = p->in_op;
+  d.nb = p->nb;
+  d.wt = p->wt;
+  d.tpw = p->tpw;
+  d.tile_rows = p->tile_rows;
+  d.n_tiles = p->n_tiles;
+  d.eps = p->eps;
+  return d;
+}
+
+__device__ __forceinline__ ChainWinDev load_win(const QG_CONST ChainWinDev *p) {
+  ChainWinDev d;
+  d.base = p->base;
+  d.x = p->x;
+  d.x2 = p->x2;
+  d.y = p->y;
+  d.row_start = p->row_start;
+  d.row_end = p->row_end;
+  return d;
+}
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int FMT>
+__global__ void __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(3)))
+chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g, const int32_t *prefix_g,
+             ChainSync *sync, unsigned base) {
+  const QG_CONST ChainStepDev *steps = (const QG_CONST ChainStepDev *)steps_g;
+  const QG_CONST ChainWinDev *wins = (const QG_CONST ChainWinDev *)wins_g;
+  const QG_CONST int32_t *prefix = (const QG_CONST int32_t *)prefix_g;
+  using F = Fmt<FMT>;
+  constexpr int BB = F::kBytes;
+  constexpr int R = TileCap<FMT, 1>::value;
+  constexpr int CH = (64 * BB + 15) / 16 + 1;  // 16-byte chunks a 64-block slice can touch
+  constexpr int V = (CH + 63) / 64;
+  constexpr int ROWB = 64 * V * 16 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kChainWaves][2][ROWB];
+  __shared__ float red[2][kChainWaves][R];
+  __shared__ float ssq[kChainWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lane16 = 16u * lane;
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+
+  // The wave's place in one step.
+  struct Role {
+    int team0;     // first wave of its team in the workgroup
+    int wit;       // its index in the team (its slice: block columns [64 wit, 64 wit + 64))
+    int tau, T;    // its team in the grid, teams in the grid
+    int my_iters;  // tiles of its team
+    int wg_iters;  // tiles of the busiest team of the workgroup
+  };
+  auto role_of = [&](const ChainStepDev &S, Role &ro) {
+    const int tiw = wid / S.wt;
+    ro.team0 = tiw * S.wt;
+    ro.wit = wid - ro.team0;
+    ro.T = G * S.tpw;
+    const int first = wg * S.tpw;
+    ro.wg_iters = S.n_tiles > first ? (S.n_tiles - first + ro.T - 1) / ro.T : 0;
+    ro.tau = first + tiw;
+    ro.my_iters = (tiw < S.tpw && ro.tau < S.n_tiles) ? (S.n_tiles - ro.tau + ro.T - 1) / ro.T : 0;
+  };
+
+  struct Tile {
+    int s, w, j;              // step, window within the step, iteration within the step
+    int64_t r0, r1, row_start;
+    const QG_GLOBAL uint8_t *rowp;  // the window's row 0 advanced to this wave's slice
+    int64_t rb;
+    uint32_t slice_len;
+    int slice_n;
+    QG_GLOBAL float *y;
+  };
+  auto locate = [&](const ChainStepDev &S, int s, int j, int t, int w_from, int wit, Tile &T) {
+    int w = w_from;
+    while (t >= prefix[S.pre0 + w + 1]) ++w;
+    const int tt = t - prefix[S.pre0 + w];
+    const ChainWinDev W = load_win(wins + S.win0 + w);
+    T.s = s;
+    T.w = w;
+    T.j = j;
+    T.row_start = W.row_start;
+    T.r0 = W.row_start + (int64_t)tt * S.tile_rows;
+    T.r1 = min(T.r0 + S.tile_rows, W.row_end);
+    T.slice_n = min(64, S.nb - 64 * wit);
+    T.rowp = (const QG_GLOBAL uint8_t *)W.base + (int64_t)(64 * wit) * BB;
+    T.rb = S.row_bytes;
+    T.slice_len = (uint32_t)(T.slice_n * BB);
+    T.y = (QG_GLOBAL float *)W.y;
+  };
+  // The tile after `cur`: the next one of its step, else the first tile of the
+  // next step in which the wave's team has work.
+  auto next_tile = [&](const Tile &cur, const Role &ro, const ChainStepDev &S, Tile &nx) -> bool {
+    if (cur.j + 1 < ro.my_iters) {
+      locate(S, cur.s, cur.j + 1, ro.tau + (cur.j + 1) * ro.T, cur.w, ro.wit, nx);
+      return true;
+    }
+    for (int s2 = cur.s + 1; s2 < n_steps; ++s2) {
+      const ChainStepDev S2 = load_step(steps + s2);
+      Role r2;
+      role_of(S2, r2);
+      if (r2.my_iters > 0) {
+        locate(S2, s2, 0, r2.tau, 0, r2.wit, nx);
+        return true;
+      }
+    }
+    return false;
+  };
+
+  u32x4 buf[R][V];
+  auto fetch_row = [&](int i, const Tile &T) {
+    const QG_GLOBAL uint8_t *p = T.rowp + min(T.r0 + i, T.r1 - 1) * T.rb;
+    const uint32_t ph = (uint32_t)((uintptr_t)p & 15);
+    const uint32_t last16 = ((ph + T.slice_len - 1) >> 4) << 4;
+    const QG_GLOBAL uint8_t *pa = p - ph;
+#pragma unroll
+    for (int v = 0; v < V; ++v) buf[i][v] = *(const QG_GLOBAL u32x4 *)(pa + min(lane16 + 1024u * v, last16));
+  };
+
+  // The 32 inputs of block column 64 wit + lane, zero past the row.
+  float xr[1][32];
+  auto load_x = [&](const float *xg, const float *x2g, bool silu, int nb, int wit) {
+    const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg;
+    const QG_GLOBAL float *x2 = (const QG_GLOBAL float *)x2g;
+    const int j = 64 * wit + lane;
+    const int jj = min(j, nb - 1);
+    const bool ok = j < nb;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      f32x4u v = *(const QG_GLOBAL f32x4u *)(x + 32 * jj + 4 * q);
+      if (silu) {
+        const f32x4u u = *(const QG_GLOBAL f32x4u *)(x2 + 32 * jj + 4 * q);
+        v.x = silu_times(v.x, u.x);
+        v.y = silu_times(v.y, u.y);
+        v.z = silu_times(v.z, u.z);
+        v.w = silu_times(v.w, u.w);
+      }
+      xr[0][4 * q + 0] = ok ? v.x : 0.0f;
+      xr[0][4 * q + 1] = ok ? v.y : 0.0f;
+      xr[0][4 * q + 2] = ok ? v.z : 0.0f;
+      xr[0][4 * q + 3] = ok ? v.w : 0.0f;
+    }
+  };
+
+  // Wave 0 runs the barrier, whose release steps wait for all of the wave's
+  // outstanding loads: it fetches a tile of a later step only after arriving
+  // at that step's barrier (`deferred`).  The other waves fetch it during
+  // their last tile of the current step.
+  Tile cur{};
+  bool deferred = false;
+  for (int s2 = 0; s2 < n_steps; ++s2) {
+    const ChainStepDev S2 = load_step(steps + s2);
+    Role r2;
+    role_of(S2, r2);
+    if (r2.my_iters > 0) {
+      locate(S2, s2, 0, r2.tau, 0, r2.wit, cur);
+#pragma unroll
+      for (int i = 0; i < R; ++i) fetch_row(i, cur);
+      break;
+    }
+  }
+  int parity = 0;
+  for (int s = 0; s < n_steps; ++s) {
+    const ChainStepDev S = load_step(steps + s);
+    Role ro;
+    role_of(S, ro);
+    const bool busy = ro.my_iters > 0;
+    if (s > 0) {
+      const unsigned target = base + (unsigned)s;
+      const bool last = chain_arrive(sync, (unsigned)G, target, wid);
+      if (deferred && cur.s == s) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) fetch_row(i, cur);
+        deferred = false;
+      }
+      chain_wait(sync, target, last, wid);
+    }
+    const bool rms = S.in_op == QG_IN_RMS || S.in_op == QG_IN_GELU_RMS;
+    int xw = -1;
+    if (rms) {
+      // Every window of an RMS step shares x: normalise it once for the step.
+      float ss = 0.0f;
+      if (busy) {
+        load_x(S.xs, nullptr, false, S.nb, ro.wit);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          if (S.in_op == QG_IN_GELU_RMS) xr[0][e] = gelu_erf(xr[0][e]);
+          ss = fmaf(xr[0][e], xr[0][e], ss);
+        }
+      }
+      ss = wave_sum63(ss);
+      if (lane == 63) ssq[wid] = ss;
+      __syncthreads();
+      if (busy) {
+        float tot = 0.0f;
+        for (int v = 0; v < S.wt; ++v) tot += ssq[ro.team0 + v];
+        const float inv = 1.0f / sqrtf(tot / (float)(32 * S.nb) + S.eps);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) xr[0][e] *= inv;
+      }
+      xw = INT32_MAX;
+    }
+    for (int j = 0; j < ro.wg_iters; ++j) {
+      const bool real = j < ro.my_iters;
+      int nrows = 0;
+      float acc[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) acc[i] = 0.0f;
+      Tile done = cur;
+      if (real) {
+        Tile nx = cur;
+        const bool more = next_tile(cur, ro, S, nx);
+        const bool now = more && (wid != 0 || nx.s == s);
+        deferred = more && !now;
+        if (xw != INT32_MAX && cur.w != xw) {
+          const ChainWinDev W = load_win(wins + S.win0 + cur.w);
+          load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
+          xw = cur.w;
+        }
+        nrows = (int)(cur.r1 - cur.r0);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          uint8_t *sb = stage[wid][i & 1];
+#pragma unroll
+          for (int v = 0; v < V; ++v) *(u32x4 *)(sb + lane16 + 1024 * v) = buf[i][v];
+          if (now) fetch_row(i, nx);
+          if (i < nrows) {
+            __builtin_amdgcn_wave_barrier();
+            const int ph = (int)((uintptr_t)(done.rowp + (done.r0 + i) * done.rb) & 15);
+            const float sp = row_partial<FMT, 1>(sb, ph, lane, done.slice_n, xr);
+            acc[i] = wave_sum63(sp);
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+        cur = nx;
+      }
+      if (S.wt == 1) {
+        if (real && lane == 63) {
+#pragma unroll
+          for (int i = 0; i < R; ++i)
+            if (i < nrows) done.y[done.r0 + i - done.row_start] = acc[i];
+        }
+      } else {
+        if (lane == 63) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) red[parity][wid][i] = acc[i];
+        }
+        __syncthreads();
+        const int tid = 64 * ro.wit + lane;
+        if (real && tid < nrows) {
+          float sum = red[parity][ro.team0][tid];
+          for (int v = 1; v < S.wt; ++v) sum += red[parity][ro.team0 + v][tid];
+          done.y[done.r0 + tid - done.row_start] = sum;
+        }
+        parity ^= 1;
+      }
+    }
   }
 }
 
@@ -694,6 +1096,7 @@ const char *qgemv_strerror(int status) {
     case QG_E_ARG: return "bad argument (block_rows, lookahead, window count, n, eps, stride, or weights not 16-byte aligned)";
     case QG_E_NOT_PINNED: return "streamed weights are not in page-locked host memory";
     case QG_E_CAPACITY: return "a row block is larger than a ring slot";
+    case QG_E_BARRIER: return "a chain's device-wide barrier gave up waiting (workgroups not co-resident)";
     case QG_E_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -944,6 +1347,211 @@ int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_windo
   if (rc) return rc;
   if (n_win == 0) return QG_OK;
   return stream_windows(st, fmt, k, win, n_win, block_rows, stream);
+}
+
+}  // extern "C"
+
+// ---- chain --------------------------------------------------------------------
+
+struct qg_chain {
+  int device;
+  int32_t fmt;
+  int32_t n_steps;
+  int grid;
+  unsigned gen;  // barrier generation at the start of the next run
+  void *mem;  // one device allocation: steps, windows, tile prefixes, barrier state
+  ChainStepDev *steps;
+  ChainWinDev *wins;
+  int32_t *prefix;
+  ChainSync *sync;
+};
+
+namespace {
+
+typedef void (*ChainFn)(const ChainStepDev *, int, const ChainWinDev *, const int32_t *, ChainSync *, unsigned);
+
+ChainFn chain_fn(int32_t fmt) {
+  switch (fmt) {
+    case QG_Q8_0: return chain_kernel<QG_Q8_0>;
+    case QG_Q4_0: return chain_kernel<QG_Q4_0>;
+    default: return chain_kernel<QG_MXFP4>;
+  }
+}
+
+bool rms_op(int32_t op) { return op == QG_IN_RMS || op == QG_IN_GELU_RMS; }
+
+int validate_chain(int32_t fmt, const qg_chain_step *steps, int32_t n_steps, const qg_chain_window *win,
+                   int32_t n_win) {
+  if (!steps || !win) return QG_E_NULL;
+  if (block_bytes(fmt) < 0) return QG_E_FMT;
+  if (n_steps < 1 || n_win < 1) return QG_E_ARG;
+  for (int i = 0; i < n_win; ++i) {
+    if (win[i].n_rows < 0) return QG_E_SHAPE;
+    int rc = check_range(win[i].n_rows, win[i].row_start, win[i].row_end);
+    if (rc) return rc;
+    if ((uintptr_t)win[i].data & 15) return QG_E_ARG;
+  }
+  for (int s = 0; s < n_steps; ++s) {
+    const qg_chain_step &S = steps[s];
+    if (S.k <= 0 || S.k % 32 != 0 || S.k > QG_CHAIN_MAX_K) return QG_E_SHAPE;
+    if (S.in_op < QG_IN_X || S.in_op > QG_IN_SILU_MUL) return QG_E_ARG;
+    if (S.n_win < 1 || S.first_win < 0 || S.first_win > n_win - S.n_win) return QG_E_ARG;
+    if (rms_op(S.in_op) && !(S.eps >= 0.0f)) return QG_E_ARG;
+    const float *xs = nullptr;
+    for (int w = S.first_win; w < S.first_win + S.n_win; ++w) {
+      const qg_chain_window &W = win[w];
+      if (W.row_end == W.row_start) continue;
+      if (!W.data || !W.x || !W.y || (S.in_op == QG_IN_SILU_MUL && !W.x2)) return QG_E_NULL;
+      if (rms_op(S.in_op)) {
+        if (xs && W.x != xs) return QG_E_ARG;
+        xs = W.x;
+      }
+    }
+  }
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps, const qg_chain_window *win,
+                       int32_t n_win, qg_chain **out) {
+  if (!out) return QG_E_NULL;
+  int rc = validate_chain(fmt, steps, n_steps, win, n_win);
+  if (rc) return rc;
+  int dev = 0, coop = 0, per_cu = 0;
+  QG_HIP(hipGetDevice(&dev));
+  QG_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  if (!coop) return hip_fail(hipErrorNotSupported, "cooperative launch");
+  const ChainFn fn = chain_fn(fmt);
+  QG_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, 64 * kChainWaves, 0));
+  if (per_cu < 1) return hip_fail(hipErrorInvalidConfiguration, "chain workgroup does not fit a compute unit");
+  const int grid = device_cus() * per_cu;
+  const int bb = block_bytes(fmt);
+  const int cap = tile_cap(fmt, 1);
+
+  std::vector<ChainWinDev> hw(n_win);
+  for (int i = 0; i < n_win; ++i)
+    hw[i] = {(const uint8_t *)win[i].data, win[i].x, win[i].x2, win[i].y, win[i].row_start, win[i].row_end};
+  std::vector<ChainStepDev> hs(n_steps);
+  std::vector<int32_t> hp;
+  for (int s = 0; s < n_steps; ++s) {
+    const qg_chain_step &S = steps[s];
+    const int nb = (int)(S.k / 32);
+    const int wt = (nb + 63) / 64;
+    const int tpw = kChainWaves / wt;
+    const int64_t teams = (int64_t)grid * tpw;
+    // Rows per tile: the fewest rows for the busiest team, with a small
+    // charge per tile (the split never changes a row's result).
+    int tr_best = 1;
+    double best = 1e300;
+    for (int tr = 1; tr <= cap; ++tr) {
+      int64_t tiles = 0;
+      for (int w = S.first_win; w < S.first_win + S.n_win; ++w)
+        tiles += (win[w].row_end - win[w].row_start + tr - 1) / tr;
+      const int64_t tpt = (tiles + teams - 1) / teams;
+      const double cost = (double)tpt * tr + 0.5 * (double)tpt;
+      if (cost < best - 1e-9) { best = cost; tr_best = tr; }
+    }
+    ChainStepDev d;
+    memset(&d, 0, sizeof(d));
+    d.pre0 = (int32_t)hp.size();
+    int64_t tiles = 0;
+    hp.push_back(0);
+    for (int w = S.first_win; w < S.first_win + S.n_win; ++w) {
+      tiles += (win[w].row_end - win[w].row_start + tr_best - 1) / tr_best;
+      if (tiles > INT32_MAX / 2) return QG_E_SHAPE;
+      hp.push_back((int32_t)tiles);
+      if (rms_op(S.in_op) && !d.xs && win[w].row_end > win[w].row_start) d.xs = win[w].x;
+    }
+    d.row_bytes = (int64_t)nb * bb;
+    d.win0 = S.first_win;
+    d.n_win = S.n_win;
+    d.in_op = S.in_op;
+    d.nb = nb;
+    d.wt = wt;
+    d.tpw = tpw;
+    d.tile_rows = tr_best;
+    d.n_tiles = (int32_t)tiles;
+    d.eps = S.eps;
+    hs[s] = d;
+  }
+  if (hp.size() > (size_t)INT32_MAX / 2) return QG_E_SHAPE;
+
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t o_steps = 0, o_wins = up(sizeof(ChainStepDev) * hs.size());
+  const size_t o_pre = o_wins + up(sizeof(ChainWinDev) * hw.size());
+  const size_t o_sync = o_pre + up(sizeof(int32_t) * hp.size());
+  const size_t total = o_sync + sizeof(ChainSync);
+  uint8_t *mem = nullptr;
+  QG_HIP(hipMalloc((void **)&mem, total));
+  auto fail = [&](hipError_t e, const char *what) {
+    (void)hipFree(mem);
+    return hip_fail(e, what);
+  };
+  hipError_t e;
+  if ((e = hipMemcpy(mem + o_steps, hs.data(), sizeof(ChainStepDev) * hs.size(), hipMemcpyHostToDevice)))
+    return fail(e, "hipMemcpy(steps)");
+  if ((e = hipMemcpy(mem + o_wins, hw.data(), sizeof(ChainWinDev) * hw.size(), hipMemcpyHostToDevice)))
+    return fail(e, "hipMemcpy(windows)");
+  if ((e = hipMemcpy(mem + o_pre, hp.data(), sizeof(int32_t) * hp.size(), hipMemcpyHostToDevice)))
+    return fail(e, "hipMemcpy(prefix)");
+  if ((e = hipMemset(mem + o_sync, 0, sizeof(ChainSync)))) return fail(e, "hipMemset(sync)");
+  if ((e = hipDeviceSynchronize())) return fail(e, "hipDeviceSynchronize");
+  qg_chain *c = new qg_chain;
+  c->device = dev;
+  c->fmt = fmt;
+  c->n_steps = n_steps;
+  c->grid = grid;
+  c->gen = 0;
+  c->mem = mem;
+  c->steps = (ChainStepDev *)(mem + o_steps);
+  c->wins = (ChainWinDev *)(mem + o_wins);
+  c->prefix = (int32_t *)(mem + o_pre);
+  c->sync = (ChainSync *)(mem + o_sync);
+  *out = c;
+  return QG_OK;
+}
+
+int qgemv_chain_run(qg_chain *c, qg_stream_t stream) {
+  if (!c) return QG_E_NULL;
+  int dev = 0;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != c->device) return QG_E_ARG;
+  unsigned base = c->gen;
+  void *args[] = {&c->steps, &c->n_steps, &c->wins, &c->prefix, &c->sync, &base};
+  QG_HIP(hipLaunchCooperativeKernel((const void *)chain_fn(c->fmt), dim3((unsigned)c->grid),
+                                    dim3(64 * kChainWaves), args, 0, stream));
+  c->gen += (unsigned)(c->n_steps - 1);
+  return QG_OK;
+}
+
+int qgemv_chain_check(qg_chain *c) {
+  if (!c) return QG_E_NULL;
+  int dev = 0;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != c->device) return QG_E_ARG;
+  QG_HIP(hipDeviceSynchronize());
+  unsigned fail = 0;
+  QG_HIP(hipMemcpy(&fail, &c->sync->fail, sizeof(fail), hipMemcpyDeviceToHost));
+  if (!fail) return QG_OK;
+  QG_HIP(hipMemset(c->sync, 0, sizeof(ChainSync)));
+  QG_HIP(hipDeviceSynchronize());
+  c->gen = 0;
+  return QG_E_BARRIER;
+}
+
+int64_t qgemv_chain_grid(const qg_chain *c) { return c ? (int64_t)c->grid : (int64_t)QG_E_NULL; }
+
+int qgemv_chain_destroy(qg_chain *c) {
+  if (!c) return QG_OK;
+  hipError_t e = hipDeviceSynchronize();
+  hipError_t f = hipFree(c->mem);
+  delete c;
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  if (f != hipSuccess) return hip_fail(f, "hipFree");
+  return QG_OK;
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qgemv.h")
 
 E_NULL, E_FMT, E_SHAPE, E_RANGE, E_SIZE, E_ARG, E_NOT_PINNED, E_CAPACITY, E_HIP = -1, -2, -3, -4, -5, -6, -7, -8, -100
+E_BARRIER = -9
 
 
 def declared():
@@ -27,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 16, names
+    assert len(names) == 21, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -42,12 +43,16 @@ def test_header_constants_match_binding():
     assert re.search(r"QG_Q8_0 = 1, QG_Q4_0 = 2, QG_MXFP4 = 3", text)
     assert f"#define QG_MAX_WINDOWS {q.MAX_WINDOWS}" in text
     assert f"#define QG_MAX_K {q.MAX_K}" in text
+    assert f"#define QG_CHAIN_MAX_K {q.CHAIN_MAX_K}" in text
+    assert re.search(rf"QG_IN_X = {q.IN_X}, QG_IN_RMS = {q.IN_RMS}, QG_IN_GELU_RMS = {q.IN_GELU_RMS}, "
+                     rf"QG_IN_SILU_MUL = {q.IN_SILU_MUL}", text)
     for code, name in q.STATUS.items():
         assert re.search(rf"{name} = {code}\b", text), name
 
 
 def test_header_compiles_as_c():
-    src = '#include "qgemv.h"\nint main(void){qg_matrix m; qg_window w; (void)m; (void)w; return 0;}\n'
+    src = ('#include "qgemv.h"\nint main(void){qg_matrix m; qg_window w; qg_chain_window cw; qg_chain_step cs;'
+           ' (void)m; (void)w; (void)cw; (void)cs; return sizeof(qg_chain_step) == 24 ? 0 : 1;}\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", f"-I{os.path.dirname(HEADER)}",
                         "-x", "c", "-"], input=src, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
@@ -191,3 +196,75 @@ def test_binding_raises_named_errors():
     with pytest.raises(q.QgemvError) as e:
         q._check(-4, "x")
     assert e.value.name == "QG_E_RANGE"
+
+
+def test_chain_struct_layout_matches_header():
+    assert ctypes.sizeof(q.qg_chain_step) == 24
+    assert ctypes.sizeof(q.qg_chain_window) == 56
+    assert q.qg_chain_window.y.offset == 48 and q.qg_chain_step.eps.offset == 20
+
+
+def cwin(r0=0, r1=8, rows=8, data=FAKE, x=FAKE, x2=0, y=FAKE):
+    return q.qg_chain_window(data, rows, r0, r1, x, x2, y)
+
+
+def cstep(k=64, first=0, n=1, op=0, eps=1e-6):
+    return q.qg_chain_step(k, first, n, op, eps)
+
+
+def test_chain_validation():
+    """Every rejection happens before any HIP call, so it runs without a GPU."""
+    L = q.lib()
+    h = ctypes.c_void_p()
+
+    def create(steps, wins, fmt=1, out=True):
+        sa = (q.qg_chain_step * max(len(steps), 1))(*steps)
+        wa = (q.qg_chain_window * max(len(wins), 1))(*wins)
+        return L.qgemv_chain_create(fmt, sa, len(steps), wa, len(wins), ctypes.byref(h) if out else None)
+
+    ok_w = [cwin(), cwin(2, 5)]
+    assert create([cstep(n=2)], ok_w, out=False) == E_NULL
+    assert L.qgemv_chain_create(1, None, 1, (q.qg_chain_window * 1)(cwin()), 1, ctypes.byref(h)) == E_NULL
+    assert create([cstep()], ok_w, fmt=4) == E_FMT
+    assert create([], ok_w) == E_ARG
+    assert create([cstep()], []) == E_ARG
+    assert create([cstep(k=48)], ok_w) == E_SHAPE
+    assert create([cstep(k=24576 + 32)], ok_w) == E_SHAPE
+    assert create([cstep(op=4)], ok_w) == E_ARG
+    assert create([cstep(op=-1)], ok_w) == E_ARG
+    assert create([cstep(n=3)], ok_w) == E_ARG  # windows past the array
+    assert create([cstep(first=-1)], ok_w) == E_ARG
+    assert create([cstep(n=0)], ok_w) == E_ARG
+    assert create([cstep(op=1, eps=-1.0)], ok_w) == E_ARG
+    assert create([cstep(op=2, eps=float("nan"))], ok_w) == E_ARG
+    assert create([cstep()], [cwin(4, 9)]) == E_RANGE
+    assert create([cstep()], [cwin(rows=-1)]) == E_SHAPE
+    assert create([cstep()], [cwin(data=FAKE + 4)]) == E_ARG
+    assert create([cstep()], [cwin(x=0)]) == E_NULL
+    assert create([cstep()], [cwin(y=0)]) == E_NULL
+    assert create([cstep()], [cwin(data=0)]) == E_NULL
+    assert create([cstep(op=3)], [cwin()]) == E_NULL  # SiLU * up needs x2
+    # the RMS transforms normalise one vector: every non-empty window shares x
+    assert create([cstep(op=1, n=2)], [cwin(), cwin(x=FAKE + 256)]) == E_ARG
+    assert L.qgemv_chain_run(None, None) == E_NULL
+    assert L.qgemv_chain_check(None) == E_NULL
+    assert L.qgemv_chain_grid(None) == E_NULL
+    assert L.qgemv_chain_destroy(None) == 0
+
+
+def test_chain_binding_checks_shapes():
+    import torch
+    w = q.Matrix(torch.zeros(8 * 2 * 34, dtype=torch.uint8), q.Q8_0, 8, 64)
+    w2 = q.Matrix(torch.zeros(8 * 4 * 34, dtype=torch.uint8), q.Q8_0, 8, 128)
+    x, y = torch.zeros(64), torch.zeros(8)
+    with pytest.raises(ValueError):
+        q._chain_tables([q.ChainStep([])])
+    with pytest.raises(ValueError):
+        q._chain_tables([q.ChainStep([q.ChainWindow(w, 0, 8, x, y), q.ChainWindow(w2, 0, 8, torch.zeros(128), y)])])
+    with pytest.raises(ValueError):
+        q._chain_tables([q.ChainStep([q.ChainWindow(w, 0, 8, torch.zeros(32), y)])])
+    sa, ns, wa, nw = q._chain_tables([q.ChainStep([q.ChainWindow(w, 0, 8, x, y)], q.IN_RMS, 1e-5),
+                                      q.ChainStep([q.ChainWindow(w, 2, 6, x, y, x2=x)], q.IN_SILU_MUL)])
+    assert (ns, nw) == (2, 2)
+    assert (sa[1].first_win, sa[1].n_win, sa[1].in_op, sa[0].k) == (1, 1, 3, 64)
+    assert wa[1].x2 == x.data_ptr() and wa[0].x2 is None
