@@ -39,25 +39,26 @@ TOL = 1e-4
 
 
 def profiled_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the kernel source as it is now; else None."""
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter
+    summary (profiles/*_hbm_traffic.md), if it was taken on the kernel source
+    as it is now; else None."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemv_q8_0_dense20b_44L_hbm_traffic.md")
     src = os.path.join(ROOT, "quantized_gemv_gguf_amd", "csrc", "qgemv.hip")
     try:
-        text = open(path).read()
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    vals = {}
-    for line in text.splitlines():
-        if "=" in line and not line.startswith(("#", "|", "`")):
-            k, v = [t.strip() for t in line.split("=", 1)]
-            vals[k] = v
-    if vals.get("kernel_source_sha256") != sha:
-        return None
-    v = vals.get(f"traffic_bytes_per_launch {kernel}")
-    return float(v) if v else None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
+        vals = {}
+        for line in open(path).read().splitlines():
+            if "=" in line and not line.startswith(("#", "|", "`")):
+                k, v = [t.strip() for t in line.split("=", 1)]
+                vals[k] = v
+        v = vals.get(f"traffic_bytes_per_launch {kernel}")
+        if v and vals.get("kernel_source_sha256") == sha:
+            return float(v)
+    return None
 
 
 def threads() -> int:
@@ -311,6 +312,8 @@ def dense_chain_workload(args, dev, model, c, layers):
         res["parity"] = dense_chain_parity(model, layers)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = dense_cpu_baseline(model, args.cpu_seconds)
+    model.chain.close()
+    torch.cuda.synchronize()
     return res
 
 

@@ -251,13 +251,17 @@ typedef struct qg_chain qg_chain;
 int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
                        const qg_chain_window *win, int32_t n_win, qg_chain **out);
 
-/* Enqueues one run of every step on `stream` (one cooperative launch on the
- * chain's device, which must be current).  Runs of one chain must not overlap:
- * they share its barrier state. */
+/* Enqueues one run of every step on `stream` (one launch on the chain's
+ * device, which must be current), of one workgroup per compute unit: all of
+ * them must be resident together, so nothing else may occupy compute units
+ * while it runs.  Runs of one chain must not overlap: they share its barrier
+ * state.  A barrier that waits longer than a few seconds gives up, and
+ * qgemv_chain_check reports it. */
 int qgemv_chain_run(qg_chain *c, qg_stream_t stream);
 
 /* Waits for the device, then QG_OK, or QG_E_BARRIER if a run's barrier gave
- * up (its outputs are then undefined; the state is reset for the next run). */
+ * up (workgroups not all resident; its outputs are then undefined, and the
+ * state is reset for the next run). */
 int qgemv_chain_check(qg_chain *c);
 
 /* Workgroups a run launches (one per compute unit), or a negative status. */

@@ -504,25 +504,35 @@ struct ChainWinDev {
   const uint8_t *base;
   const float *x, *x2;
   float *y;
+  float *act;  // if set, also receives gelu(y) (the next step's GELU, done once per row)
   int64_t row_start, row_end;
 };
 
+// Everything a step needs is in its record, its first window included, so a
+// single-window step reads no table after the record.
 struct ChainStepDev {
+  ChainWinDev w0;   // the step's first window
   const float *xs;  // the RMS ops' shared x (first non-empty window's)
   int64_t row_bytes;
+  uint64_t team_of_wave;  // 4 bits per wave: its team in the workgroup, 15 = none
   int32_t win0, n_win, pre0;  // windows [win0, win0 + n_win); their tile prefix at pre0
   int32_t in_op, nb, wt, tpw, tile_rows, n_tiles;
+  int32_t teams;           // teams in the grid (workgroups * tpw)
+  int32_t iters_q, iters_r;  // n_tiles = iters_q * teams + iters_r
   float eps;
 };
 
 // Barrier state, one 256-byte line per word.  `count` returns to 0 after every
-// barrier and `gen` only grows (wrapping): barrier b of a launch is complete
-// once gen reaches base + b, base being gen at the launch's start, which the
-// host tracks from run to run.
+// barrier; each workgroup polls a generation of its own line (spreading the
+// polls over as many lines), which only grows (wrapping): barrier b of a launch
+// is complete once it reaches base + b, base being the generation at the
+// launch's start, which the host tracks from run to run.
+constexpr int kMaxChainGroups = 1024;
+
 struct ChainSync {
   unsigned count, pad0[63];
-  unsigned gen, pad1[63];
-  unsigned fail, pad2[63];
+  unsigned fail, pad1[63];
+  struct { unsigned gen, pad[63]; } flag[kMaxChainGroups];  // one line per workgroup
 };
 
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained
@@ -535,8 +545,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt u
 //   arrive: release fence (L2 write-back of the workgroup's stores; the
 //     compiler's own wait after it can be dropped when nothing else is
 //     outstanding, so an explicit one follows), then add 1 to `count`.  The
-//     last arrival acquires, resets `count`, releases, and publishes `target`.
-//   wait: unless last, poll `gen` until it reaches `target`, then acquire.
+//     last arrival acquires, resets `count`, releases, and writes `target`
+//     to every workgroup's line.
+//   wait: unless last, poll the own line until it reaches `target`, then
+//     acquire.
 // A barrier still incomplete after kSpinLimit polls marks `fail` and lets the
 // workgroup through, so the kernel always ends; the host reports it.
 __device__ __forceinline__ bool chain_arrive(ChainSync *sy, unsigned n_groups, unsigned target, int wid) {
@@ -553,7 +565,8 @@ __device__ __forceinline__ bool chain_arrive(ChainSync *sy, unsigned n_groups, u
       __hip_atomic_store(&sy->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __hip_atomic_store(&sy->gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (unsigned g = threadIdx.x & 63; g < n_groups; g += 64)
+        __hip_atomic_store(&sy->flag[g].gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   return last;
@@ -562,8 +575,8 @@ __device__ __forceinline__ bool chain_arrive(ChainSync *sy, unsigned n_groups, u
 __device__ __forceinline__ void chain_wait(ChainSync *sy, unsigned target, bool last, int wid) {
   if (wid == 0 && !last) {
     for (unsigned spins = 1;; ++spins) {
-      const unsigned g =
-          __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sy->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const unsigned g = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&sy->flag[blockIdx.x].gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       if ((int)(g - target) >= 0) break;
       if ((spins & 63) == 0) {
         const unsigned f = __builtin_amdgcn_readfirstlane(
@@ -593,10 +606,25 @@ __device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f
 // barrier's fences they would be vector loads, each draining the prefetch).
 #define QG_CONST __attribute__((address_space(4)))
 
+
+__device__ __forceinline__ ChainWinDev load_win(const QG_CONST ChainWinDev *p) {
+  ChainWinDev d;
+  d.base = p->base;
+  d.x = p->x;
+  d.x2 = p->x2;
+  d.y = p->y;
+  d.act = p->act;
+  d.row_start = p->row_start;
+  d.row_end = p->row_end;
+  return d;
+}
+
 __device__ __forceinline__ ChainStepDev load_step(const QG_CONST ChainStepDev *p) {
   ChainStepDev d;
+  d.w0 = load_win(&p->w0);
   d.xs = p->xs;
   d.row_bytes = p->row_bytes;
+  d.team_of_wave = p->team_of_wave;
   d.win0 = p->win0;
   d.n_win = p->n_win;
   d.pre0 = p->pre0;
@@ -606,18 +634,10 @@ __device__ __forceinline__ ChainStepDev load_step(const QG_CONST ChainStepDev *p
   d.tpw = p->tpw;
   d.tile_rows = p->tile_rows;
   d.n_tiles = p->n_tiles;
+  d.teams = p->teams;
+  d.iters_q = p->iters_q;
+  d.iters_r = p->iters_r;
   d.eps = p->eps;
-  return d;
-}
-
-__device__ __forceinline__ ChainWinDev load_win(const QG_CONST ChainWinDev *p) {
-  ChainWinDev d;
-  d.base = p->base;
-  d.x = p->x;
-  d.x2 = p->x2;
-  d.y = p->y;
-  d.row_start = p->row_start;
-  d.row_end = p->row_end;
   return d;
 }
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
@@ -653,15 +673,18 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     int my_iters;  // tiles of its team
     int wg_iters;  // tiles of the busiest team of the workgroup
   };
+  // Team tau takes tiles tau, tau + T, ...: iters_q of them, one more if
+  // tau < iters_r.  The workgroup's first team has the most.
   auto role_of = [&](const ChainStepDev &S, Role &ro) {
-    const int tiw = wid / S.wt;
-    ro.team0 = tiw * S.wt;
+    const int tiw = (int)((S.team_of_wave >> (4 * wid)) & 15);
+    const bool member = tiw != 15;
+    ro.team0 = member ? tiw * S.wt : wid;
     ro.wit = wid - ro.team0;
-    ro.T = G * S.tpw;
+    ro.T = S.teams;
     const int first = wg * S.tpw;
-    ro.wg_iters = S.n_tiles > first ? (S.n_tiles - first + ro.T - 1) / ro.T : 0;
-    ro.tau = first + tiw;
-    ro.my_iters = (tiw < S.tpw && ro.tau < S.n_tiles) ? (S.n_tiles - ro.tau + ro.T - 1) / ro.T : 0;
+    ro.wg_iters = S.iters_q + (first < S.iters_r ? 1 : 0);
+    ro.tau = first + (member ? tiw : 0);
+    ro.my_iters = member ? S.iters_q + (ro.tau < S.iters_r ? 1 : 0) : 0;
   };
 
   struct Tile {
@@ -672,12 +695,17 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     uint32_t slice_len;
     int slice_n;
     QG_GLOBAL float *y;
+    QG_GLOBAL float *act;
   };
   auto locate = [&](const ChainStepDev &S, int s, int j, int t, int w_from, int wit, Tile &T) {
-    int w = w_from;
-    while (t >= prefix[S.pre0 + w + 1]) ++w;
-    const int tt = t - prefix[S.pre0 + w];
-    const ChainWinDev W = load_win(wins + S.win0 + w);
+    int w = 0, tt = t;
+    ChainWinDev W = S.w0;
+    if (S.n_win > 1) {
+      w = w_from;
+      while (t >= prefix[S.pre0 + w + 1]) ++w;
+      tt = t - prefix[S.pre0 + w];
+      W = load_win(wins + S.win0 + w);
+    }
     T.s = s;
     T.w = w;
     T.j = j;
@@ -689,6 +717,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     T.rb = S.row_bytes;
     T.slice_len = (uint32_t)(T.slice_n * BB);
     T.y = (QG_GLOBAL float *)W.y;
+    T.act = (QG_GLOBAL float *)W.act;
   };
   // The tile after `cur`: the next one of its step, else the first tile of the
   // next step in which the wave's team has work.
@@ -815,7 +844,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         const bool now = more && (wid != 0 || nx.s == s);
         deferred = more && !now;
         if (xw != INT32_MAX && cur.w != xw) {
-          const ChainWinDev W = load_win(wins + S.win0 + cur.w);
+          const ChainWinDev W = S.n_win > 1 ? load_win(wins + S.win0 + cur.w) : S.w0;
           load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
           xw = cur.w;
         }
@@ -840,7 +869,10 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         if (real && lane == 63) {
 #pragma unroll
           for (int i = 0; i < R; ++i)
-            if (i < nrows) done.y[done.r0 + i - done.row_start] = acc[i];
+            if (i < nrows) {
+              done.y[done.r0 + i - done.row_start] = acc[i];
+              if (done.act) done.act[done.r0 + i - done.row_start] = gelu_erf(acc[i]);
+            }
         }
       } else {
         if (lane == 63) {
@@ -853,6 +885,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
           float sum = red[parity][ro.team0][tid];
           for (int v = 1; v < S.wt; ++v) sum += red[parity][ro.team0 + v][tid];
           done.y[done.r0 + tid - done.row_start] = sum;
+          if (done.act) done.act[done.r0 + tid - done.row_start] = gelu_erf(sum);
         }
         parity ^= 1;
       }
@@ -1420,20 +1453,18 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
   if (!out) return QG_E_NULL;
   int rc = validate_chain(fmt, steps, n_steps, win, n_win);
   if (rc) return rc;
-  int dev = 0, coop = 0, per_cu = 0;
+  int dev = 0, per_cu = 0;
   QG_HIP(hipGetDevice(&dev));
-  QG_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
-  if (!coop) return hip_fail(hipErrorNotSupported, "cooperative launch");
   const ChainFn fn = chain_fn(fmt);
   QG_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, 64 * kChainWaves, 0));
   if (per_cu < 1) return hip_fail(hipErrorInvalidConfiguration, "chain workgroup does not fit a compute unit");
-  const int grid = device_cus() * per_cu;
+  const int grid = std::min(device_cus() * per_cu, kMaxChainGroups);
   const int bb = block_bytes(fmt);
   const int cap = tile_cap(fmt, 1);
 
   std::vector<ChainWinDev> hw(n_win);
   for (int i = 0; i < n_win; ++i)
-    hw[i] = {(const uint8_t *)win[i].data, win[i].x, win[i].x2, win[i].y, win[i].row_start, win[i].row_end};
+    hw[i] = {(const uint8_t *)win[i].data, win[i].x, win[i].x2, win[i].y, nullptr, win[i].row_start, win[i].row_end};
   std::vector<ChainStepDev> hs(n_steps);
   std::vector<int32_t> hp;
   for (int s = 0; s < n_steps; ++s) {
@@ -1465,7 +1496,12 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
       hp.push_back((int32_t)tiles);
       if (rms_op(S.in_op) && !d.xs && win[w].row_end > win[w].row_start) d.xs = win[w].x;
     }
+    d.w0 = hw[S.first_win];
     d.row_bytes = (int64_t)nb * bb;
+    d.team_of_wave = 0;
+    for (int v = 0; v < kChainWaves; ++v)
+      d.team_of_wave |= (uint64_t)(v / wt < tpw ? v / wt : 15) << (4 * v);
+    d.teams = (int32_t)teams;
     d.win0 = S.first_win;
     d.n_win = S.n_win;
     d.in_op = S.in_op;
@@ -1474,18 +1510,46 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
     d.tpw = tpw;
     d.tile_rows = tr_best;
     d.n_tiles = (int32_t)tiles;
+    d.iters_q = (int32_t)(tiles / teams);
+    d.iters_r = (int32_t)(tiles % teams);
     d.eps = S.eps;
     hs[s] = d;
   }
   if (hp.size() > (size_t)INT32_MAX / 2) return QG_E_SHAPE;
+  // A GELU + RMS step whose x is the whole output of one window of the step
+  // before it gets gelu(x) from that window's stores (computed once per row
+  // instead of once per team), into a buffer of the chain, and normalises it.
+  std::vector<std::pair<int, int>> gelu_feed;  // (producing window, consuming step)
+  for (int s = 1; s < n_steps; ++s) {
+    if (hs[s].in_op != QG_IN_GELU_RMS || !hs[s].xs) continue;
+    const qg_chain_step &P = steps[s - 1];
+    for (int w = P.first_win; w < P.first_win + P.n_win; ++w)
+      if (win[w].y == hs[s].xs && win[w].row_end - win[w].row_start == steps[s].k) {
+        gelu_feed.push_back({w, s});
+        break;
+      }
+  }
 
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t o_steps = 0, o_wins = up(sizeof(ChainStepDev) * hs.size());
   const size_t o_pre = o_wins + up(sizeof(ChainWinDev) * hw.size());
   const size_t o_sync = o_pre + up(sizeof(int32_t) * hp.size());
-  const size_t total = o_sync + sizeof(ChainSync);
+  size_t o_act = o_sync + up(sizeof(ChainSync));
+  std::vector<size_t> act_off(n_win, 0);  // offset of a window's gelu buffer, 0 = none
+  for (auto &f : gelu_feed)
+    if (!act_off[f.first]) {
+      act_off[f.first] = o_act;
+      o_act += up(sizeof(float) * steps[f.second].k);
+    }
+  const size_t total = o_act;
   uint8_t *mem = nullptr;
   QG_HIP(hipMalloc((void **)&mem, total));
+  for (auto &f : gelu_feed) {
+    hw[f.first].act = (float *)(mem + act_off[f.first]);
+    hs[f.second].in_op = QG_IN_RMS;
+    hs[f.second].xs = hw[f.first].act;
+  }
+  for (int s = 0; s < n_steps; ++s) hs[s].w0 = hw[steps[s].first_win];
   auto fail = [&](hipError_t e, const char *what) {
     (void)hipFree(mem);
     return hip_fail(e, what);
@@ -1519,10 +1583,13 @@ int qgemv_chain_run(qg_chain *c, qg_stream_t stream) {
   int dev = 0;
   QG_HIP(hipGetDevice(&dev));
   if (dev != c->device) return QG_E_ARG;
-  unsigned base = c->gen;
-  void *args[] = {&c->steps, &c->n_steps, &c->wins, &c->prefix, &c->sync, &base};
-  QG_HIP(hipLaunchCooperativeKernel((const void *)chain_fn(c->fmt), dim3((unsigned)c->grid),
-                                    dim3(64 * kChainWaves), args, 0, stream));
+  // An ordinary launch of exactly as many workgroups as the device holds at
+  // once, so on a device running nothing else every workgroup is resident.
+  // (Should one not be, the barrier gives up after a bounded wait instead of
+  // hanging, and qgemv_chain_check reports it.)
+  hipLaunchKernelGGL(chain_fn(c->fmt), dim3((unsigned)c->grid), dim3(64 * kChainWaves), 0, stream, c->steps,
+                     c->n_steps, c->wins, c->prefix, c->sync, c->gen);
+  QG_HIP(hipGetLastError());
   c->gen += (unsigned)(c->n_steps - 1);
   return QG_OK;
 }
