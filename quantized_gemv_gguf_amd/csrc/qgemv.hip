@@ -605,6 +605,7 @@ __device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f
 // nor hold up the vector loads of the weights (as plain global loads after the
 // barrier's fences they would be vector loads, each draining the prefetch).
 #define QG_CONST __attribute__((address_space(4)))
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 
 
 __device__ __forceinline__ ChainWinDev load_win(const QG_CONST ChainWinDev *p) {
@@ -640,7 +641,6 @@ __device__ __forceinline__ ChainStepDev load_step(const QG_CONST ChainStepDev *p
   d.eps = p->eps;
   return d;
 }
-typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int FMT>
 __global__ void __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(3)))
@@ -656,7 +656,15 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   constexpr int V = (CH + 63) / 64;
   constexpr int ROWB = 64 * V * 16 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t stage[kChainWaves][2][ROWB];
-  __shared__ float red[2][kChainWaves][R];
+  // Team reduction ring (several teams per workgroup): a wave writes its row
+  // sums for tile j into slot j % kRing and counts itself in; the last of the
+  // team to arrive adds them in wave order, stores y and marks the slot
+  // consumed.  No workgroup-wide sync per tile, so the teams of a workgroup
+  // do not wait for each other.  A team that is the whole workgroup uses the
+  // workgroup barrier and two of the slots instead.
+  constexpr int kRing = 4;
+  __shared__ float red[kRing][kChainWaves][R];
+  __shared__ unsigned arrived[kChainWaves][kRing], consumed[kChainWaves][kRing];
   __shared__ float ssq[kChainWaves];
 
   const int lane = threadIdx.x & 63;
@@ -671,10 +679,9 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     int wit;       // its index in the team (its slice: block columns [64 wit, 64 wit + 64))
     int tau, T;    // its team in the grid, teams in the grid
     int my_iters;  // tiles of its team
-    int wg_iters;  // tiles of the busiest team of the workgroup
   };
   // Team tau takes tiles tau, tau + T, ...: iters_q of them, one more if
-  // tau < iters_r.  The workgroup's first team has the most.
+  // tau < iters_r.
   auto role_of = [&](const ChainStepDev &S, Role &ro) {
     const int tiw = (int)((S.team_of_wave >> (4 * wid)) & 15);
     const bool member = tiw != 15;
@@ -682,7 +689,6 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     ro.wit = wid - ro.team0;
     ro.T = S.teams;
     const int first = wg * S.tpw;
-    ro.wg_iters = S.iters_q + (first < S.iters_r ? 1 : 0);
     ro.tau = first + (member ? tiw : 0);
     ro.my_iters = member ? S.iters_q + (ro.tau < S.iters_r ? 1 : 0) : 0;
   };
@@ -790,7 +796,17 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
       break;
     }
   }
-  int parity = 0;
+  // Ring counters restart with every step (its teams differ); every wave is
+  // past the previous step's tile loop here (the barrier's workgroup sync),
+  // and none enters the next before the sync that ends the barrier.
+  auto reset_ring = [&]() {
+    if (threadIdx.x < kChainWaves * kRing) {
+      (&arrived[0][0])[threadIdx.x] = 0;
+      (&consumed[0][0])[threadIdx.x] = 0;
+    }
+  };
+  reset_ring();
+  __syncthreads();
   for (int s = 0; s < n_steps; ++s) {
     const ChainStepDev S = load_step(steps + s);
     Role ro;
@@ -799,6 +815,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     if (s > 0) {
       const unsigned target = base + (unsigned)s;
       const bool last = chain_arrive(sync, (unsigned)G, target, wid);
+      reset_ring();
       if (deferred && cur.s == s) {
 #pragma unroll
         for (int i = 0; i < R; ++i) fetch_row(i, cur);
@@ -831,42 +848,39 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
       }
       xw = INT32_MAX;
     }
-    for (int j = 0; j < ro.wg_iters; ++j) {
-      const bool real = j < ro.my_iters;
-      int nrows = 0;
+    const int tiw = ro.team0 / max(S.wt, 1);
+    for (int j = 0; j < ro.my_iters; ++j) {
       float acc[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) acc[i] = 0.0f;
-      Tile done = cur;
-      if (real) {
-        Tile nx = cur;
-        const bool more = next_tile(cur, ro, S, nx);
-        const bool now = more && (wid != 0 || nx.s == s);
-        deferred = more && !now;
-        if (xw != INT32_MAX && cur.w != xw) {
-          const ChainWinDev W = S.n_win > 1 ? load_win(wins + S.win0 + cur.w) : S.w0;
-          load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
-          xw = cur.w;
-        }
-        nrows = (int)(cur.r1 - cur.r0);
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          uint8_t *sb = stage[wid][i & 1];
-#pragma unroll
-          for (int v = 0; v < V; ++v) *(u32x4 *)(sb + lane16 + 1024 * v) = buf[i][v];
-          if (now) fetch_row(i, nx);
-          if (i < nrows) {
-            __builtin_amdgcn_wave_barrier();
-            const int ph = (int)((uintptr_t)(done.rowp + (done.r0 + i) * done.rb) & 15);
-            const float sp = row_partial<FMT, 1>(sb, ph, lane, done.slice_n, xr);
-            acc[i] = wave_sum63(sp);
-            __builtin_amdgcn_wave_barrier();
-          }
-        }
-        cur = nx;
+      const Tile done = cur;
+      Tile nx = cur;
+      const bool more = next_tile(cur, ro, S, nx);
+      const bool now = more && (wid != 0 || nx.s == s);
+      deferred = more && !now;
+      if (xw != INT32_MAX && cur.w != xw) {
+        const ChainWinDev W = S.n_win > 1 ? load_win(wins + S.win0 + cur.w) : S.w0;
+        load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
+        xw = cur.w;
       }
+      const int nrows = (int)(cur.r1 - cur.r0);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        uint8_t *sb = stage[wid][i & 1];
+#pragma unroll
+        for (int v = 0; v < V; ++v) *(u32x4 *)(sb + lane16 + 1024 * v) = buf[i][v];
+        if (now) fetch_row(i, nx);
+        if (i < nrows) {
+          __builtin_amdgcn_wave_barrier();
+          const int ph = (int)((uintptr_t)(done.rowp + (done.r0 + i) * done.rb) & 15);
+          const float sp = row_partial<FMT, 1>(sb, ph, lane, done.slice_n, xr);
+          acc[i] = wave_sum63(sp);
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+      cur = nx;
       if (S.wt == 1) {
-        if (real && lane == 63) {
+        if (lane == 63) {
 #pragma unroll
           for (int i = 0; i < R; ++i)
             if (i < nrows) {
@@ -874,20 +888,45 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
               if (done.act) done.act[done.r0 + i - done.row_start] = gelu_erf(acc[i]);
             }
         }
-      } else {
+      } else if (S.tpw == 1) {
+        // One team per workgroup: the hardware barrier is cheaper than the ring.
         if (lane == 63) {
 #pragma unroll
-          for (int i = 0; i < R; ++i) red[parity][wid][i] = acc[i];
+          for (int i = 0; i < R; ++i) red[j & 1][wid][i] = acc[i];
         }
         __syncthreads();
-        const int tid = 64 * ro.wit + lane;
-        if (real && tid < nrows) {
-          float sum = red[parity][ro.team0][tid];
-          for (int v = 1; v < S.wt; ++v) sum += red[parity][ro.team0 + v][tid];
-          done.y[done.r0 + tid - done.row_start] = sum;
-          if (done.act) done.act[done.r0 + tid - done.row_start] = gelu_erf(sum);
+        if (wid == 0 && lane < nrows) {
+          float sum = red[j & 1][0][lane];
+          for (int v = 1; v < S.wt; ++v) sum += red[j & 1][v][lane];
+          done.y[done.r0 + lane - done.row_start] = sum;
+          if (done.act) done.act[done.r0 + lane - done.row_start] = gelu_erf(sum);
         }
-        parity ^= 1;
+      } else {
+        const int slot = j & (kRing - 1);
+        const unsigned use = (unsigned)(j / kRing);
+        // The slot's previous use must have been read (waits only when this
+        // wave runs kRing tiles ahead of its team's slowest).
+        while (__builtin_amdgcn_readfirstlane(
+                   __hip_atomic_load(&consumed[tiw][slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < use)
+          __builtin_amdgcn_s_sleep(1);
+        unsigned before = 0;
+        if (lane == 63) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) red[slot][wid][i] = acc[i];
+          before = __hip_atomic_fetch_add(&arrived[tiw][slot], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        before = __builtin_amdgcn_readlane(before, 63);
+        if (before == (use + 1) * (unsigned)S.wt - 1) {
+          // Last of the team: every partial of this tile is in the slot.
+          if (lane < nrows) {
+            float sum = red[slot][ro.team0][lane];
+            for (int v = 1; v < S.wt; ++v) sum += red[slot][ro.team0 + v][lane];
+            done.y[done.r0 + lane - done.row_start] = sum;
+            if (done.act) done.act[done.r0 + lane - done.row_start] = gelu_erf(sum);
+          }
+          __builtin_amdgcn_wave_barrier();
+          if (lane == 0) __hip_atomic_store(&consumed[tiw][slot], use + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
     }
   }
