@@ -754,8 +754,45 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     for (int v = 0; v < V; ++v) buf[i][v] = *(const QG_GLOBAL u32x4 *)(pa + min(lane16 + 1024u * v, last16));
   };
 
-  // The 32 inputs of block column 64 wit + lane, zero past the row.
+  // The 32 inputs of block column 64 wit + lane, zero past the row.  Once per
+  // step (the RMS steps' shared x), the wave's 2048-float slice of x is read
+  // with contiguous 1 KB loads (lane l takes floats 4(l + 64q) .. + 4, q < 8)
+  // and turned around in the wave's staging buffer, in two halves of 4 KB: a
+  // lane's own 128 contiguous bytes read directly make every load touch 64
+  // cache lines, and when every workgroup reads x at once right after the
+  // barrier those requests queue for microseconds.
   float xr[1][32];
+  auto gather_x = [&](const float *xg, int nb, int wit, float (&out)[32]) {
+    const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg + 2048 * wit;
+    const int nf = min(2048, 32 * (nb - 64 * wit));  // floats of x in the slice
+    f32x4u t[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int off = 4 * (lane + 64 * q);
+      const f32x4u v = *(const QG_GLOBAL f32x4u *)(x + min(off, nf - 4));
+      t[q] = off < nf ? v : f32x4u{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    uint8_t *sb = stage[wid][0];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *(f32x4u *)(sb + 16 * (lane + 64 * q)) = t[4 * half + q];
+      __builtin_amdgcn_wave_barrier();
+      if ((lane >> 5) == half) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x4u v = *(const f32x4u *)(sb + 128 * (lane & 31) + 16 * e);
+          out[4 * e + 0] = v.x;
+          out[4 * e + 1] = v.y;
+          out[4 * e + 2] = v.z;
+          out[4 * e + 3] = v.w;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  // Per window (inside the tile loop, where the current tile's weights are
+  // live in registers): each lane loads its own inputs directly.
   auto load_x = [&](const float *xg, const float *x2g, bool silu, int nb, int wit) {
     const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg;
     const QG_GLOBAL float *x2 = (const QG_GLOBAL float *)x2g;
@@ -829,7 +866,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
       // Every window of an RMS step shares x: normalise it once for the step.
       float ss = 0.0f;
       if (busy) {
-        load_x(S.xs, nullptr, false, S.nb, ro.wit);
+        gather_x(S.xs, S.nb, ro.wit, xr[0]);
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
           if (S.in_op == QG_IN_GELU_RMS) xr[0][e] = gelu_erf(xr[0][e]);
