@@ -483,8 +483,9 @@ rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
 // ---------------------------------------------------------------------------
 //
 // One workgroup of kChainWaves waves per CU stays resident for the whole
-// chain.  In each step a team is ceil(nb/64) of those waves (one block column
-// per lane, as in gemv_kernel with C = 1), a workgroup holds 12 / WT teams,
+// chain.  In each step a team is ceil(nb/64C) of those waves with the lane
+// to block map of gemv_kernel at the same (format, k): C = 1 block column per
+// lane for Q8_0, 2 for Q4_0 and MXFP4.  A workgroup holds 12 / WT teams,
 // and team tau of the grid takes tiles tau, tau + T, tau + 2T, ...  Between
 // steps every workgroup waits at a device-wide barrier, because the next
 // step's input is the previous step's output.  Weights never depend on it:
@@ -498,6 +499,10 @@ rms_carry_kernel(const float *v, float *out, int64_t n, float eps, int gelu) {
 // so a chain reproduces the separate calls bit for bit.
 
 constexpr int kChainWaves = 12;
+
+// Rows per chain tile: the tile cap of gemv_kernel, one row less at two
+// columns per lane (the chain keeps more state in registers).
+template <int FMT, int C> struct ChainRows { static constexpr int value = TileCap<FMT, C>::value - (C == 2 ? 1 : 0); };
 constexpr unsigned kSpinLimit = 1u << 22;  // barrier polls before giving up (seconds)
 
 struct ChainWinDev {
@@ -642,7 +647,7 @@ __device__ __forceinline__ ChainStepDev load_step(const QG_CONST ChainStepDev *p
   return d;
 }
 
-template <int FMT>
+template <int FMT, int C>
 __global__ void __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(3)))
 chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g, const int32_t *prefix_g,
              ChainSync *sync, unsigned base) {
@@ -651,8 +656,9 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   const QG_CONST int32_t *prefix = (const QG_CONST int32_t *)prefix_g;
   using F = Fmt<FMT>;
   constexpr int BB = F::kBytes;
-  constexpr int R = TileCap<FMT, 1>::value;
-  constexpr int CH = (64 * BB + 15) / 16 + 1;  // 16-byte chunks a 64-block slice can touch
+  constexpr int R = ChainRows<FMT, C>::value;
+  constexpr int SB = 64 * C;                   // blocks per wave slice
+  constexpr int CH = (SB * BB + 15) / 16 + 1;  // 16-byte chunks a slice can touch
   constexpr int V = (CH + 63) / 64;
   constexpr int ROWB = 64 * V * 16 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t stage[kChainWaves][2][ROWB];
@@ -665,7 +671,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   constexpr int kRing = 4;
   __shared__ float red[kRing][kChainWaves][R];
   __shared__ unsigned arrived[kChainWaves][kRing], consumed[kChainWaves][kRing];
-  __shared__ float ssq[kChainWaves];
+  __shared__ float ssq[kChainWaves * C];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -718,8 +724,8 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     T.row_start = W.row_start;
     T.r0 = W.row_start + (int64_t)tt * S.tile_rows;
     T.r1 = min(T.r0 + S.tile_rows, W.row_end);
-    T.slice_n = min(64, S.nb - 64 * wit);
-    T.rowp = (const QG_GLOBAL uint8_t *)W.base + (int64_t)(64 * wit) * BB;
+    T.slice_n = min(SB, S.nb - SB * wit);
+    T.rowp = (const QG_GLOBAL uint8_t *)W.base + (int64_t)(SB * wit) * BB;
     T.rb = S.row_bytes;
     T.slice_len = (uint32_t)(T.slice_n * BB);
     T.y = (QG_GLOBAL float *)W.y;
@@ -754,22 +760,22 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     for (int v = 0; v < V; ++v) buf[i][v] = *(const QG_GLOBAL u32x4 *)(pa + min(lane16 + 1024u * v, last16));
   };
 
-  // The 32 inputs of block column 64 wit + lane, zero past the row.  Once per
-  // step (the RMS steps' shared x), the wave's 2048-float slice of x is read
-  // with contiguous 1 KB loads (lane l takes floats 4(l + 64q) .. + 4, q < 8)
-  // and turned around in the wave's staging buffer, in two halves of 4 KB: a
-  // lane's own 128 contiguous bytes read directly make every load touch 64
-  // cache lines, and when every workgroup reads x at once right after the
-  // barrier those requests queue for microseconds.
-  float xr[1][32];
-  auto gather_x = [&](const float *xg, int nb, int wit, float (&out)[32]) {
-    const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg + 2048 * wit;
-    const int nf = min(2048, 32 * (nb - 64 * wit));  // floats of x in the slice
+  // The 32 inputs of each block column SB wit + 64 c + lane, zero past the
+  // row.  Once per step (the RMS steps' shared x), each 2048-float run of the
+  // wave's slice is read with contiguous 1 KB loads (lane l takes floats
+  // 4(l + 64q) .. + 4, q < 8) and turned around in the wave's staging buffer,
+  // in two halves of 4 KB: a lane's own 128 contiguous bytes read directly
+  // make every load touch 64 cache lines, and when every workgroup reads x at
+  // once right after the barrier those requests queue for microseconds.
+  float xr[C][32];
+  auto gather_x = [&](const float *xg, int b0, int nb, float (&out)[32]) {
+    const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg + 32 * min(b0, nb - 1);
+    const int nf = 32 * min(64, nb - b0);  // floats of x in the run (<= 0: none)
     f32x4u t[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int off = 4 * (lane + 64 * q);
-      const f32x4u v = *(const QG_GLOBAL f32x4u *)(x + min(off, nf - 4));
+      const f32x4u v = *(const QG_GLOBAL f32x4u *)(x + min(off, max(nf, 4) - 4));
       t[q] = off < nf ? v : f32x4u{0.0f, 0.0f, 0.0f, 0.0f};
     }
     uint8_t *sb = stage[wid][0];
@@ -796,23 +802,26 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   auto load_x = [&](const float *xg, const float *x2g, bool silu, int nb, int wit) {
     const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg;
     const QG_GLOBAL float *x2 = (const QG_GLOBAL float *)x2g;
-    const int j = 64 * wit + lane;
-    const int jj = min(j, nb - 1);
-    const bool ok = j < nb;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      f32x4u v = *(const QG_GLOBAL f32x4u *)(x + 32 * jj + 4 * q);
-      if (silu) {
-        const f32x4u u = *(const QG_GLOBAL f32x4u *)(x2 + 32 * jj + 4 * q);
-        v.x = silu_times(v.x, u.x);
-        v.y = silu_times(v.y, u.y);
-        v.z = silu_times(v.z, u.z);
-        v.w = silu_times(v.w, u.w);
+    for (int c = 0; c < C; ++c) {
+      const int j = SB * wit + 64 * c + lane;
+      const int jj = min(j, nb - 1);
+      const bool ok = j < nb;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        f32x4u v = *(const QG_GLOBAL f32x4u *)(x + 32 * jj + 4 * q);
+        if (silu) {
+          const f32x4u u = *(const QG_GLOBAL f32x4u *)(x2 + 32 * jj + 4 * q);
+          v.x = silu_times(v.x, u.x);
+          v.y = silu_times(v.y, u.y);
+          v.z = silu_times(v.z, u.z);
+          v.w = silu_times(v.w, u.w);
+        }
+        xr[c][4 * q + 0] = ok ? v.x : 0.0f;
+        xr[c][4 * q + 1] = ok ? v.y : 0.0f;
+        xr[c][4 * q + 2] = ok ? v.z : 0.0f;
+        xr[c][4 * q + 3] = ok ? v.w : 0.0f;
       }
-      xr[0][4 * q + 0] = ok ? v.x : 0.0f;
-      xr[0][4 * q + 1] = ok ? v.y : 0.0f;
-      xr[0][4 * q + 2] = ok ? v.z : 0.0f;
-      xr[0][4 * q + 3] = ok ? v.w : 0.0f;
     }
   };
 
@@ -864,24 +873,31 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     int xw = -1;
     if (rms) {
       // Every window of an RMS step shares x: normalise it once for the step.
-      float ss = 0.0f;
-      if (busy) {
-        gather_x(S.xs, S.nb, ro.wit, xr[0]);
+      // Column c of a lane's blocks is its own 64-block run, summed like one
+      // wave of qgemv_rms_carry; the runs are then added in column order.
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          if (S.in_op == QG_IN_GELU_RMS) xr[0][e] = gelu_erf(xr[0][e]);
-          ss = fmaf(xr[0][e], xr[0][e], ss);
+      for (int c = 0; c < C; ++c) {
+        float ss = 0.0f;
+        if (busy) {
+          gather_x(S.xs, SB * ro.wit + 64 * c, S.nb, xr[c]);
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            if (S.in_op == QG_IN_GELU_RMS) xr[c][e] = gelu_erf(xr[c][e]);
+            ss = fmaf(xr[c][e], xr[c][e], ss);
+          }
         }
+        ss = wave_sum63(ss);
+        if (lane == 63) ssq[C * wid + c] = ss;
       }
-      ss = wave_sum63(ss);
-      if (lane == 63) ssq[wid] = ss;
       __syncthreads();
       if (busy) {
         float tot = 0.0f;
-        for (int v = 0; v < S.wt; ++v) tot += ssq[ro.team0 + v];
+        for (int v = 0; v < C * S.wt; ++v) tot += ssq[C * ro.team0 + v];
         const float inv = 1.0f / sqrtf(tot / (float)(32 * S.nb) + S.eps);
 #pragma unroll
-        for (int e = 0; e < 32; ++e) xr[0][e] *= inv;
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+          for (int e = 0; e < 32; ++e) xr[c][e] *= inv;
       }
       xw = INT32_MAX;
     }
@@ -910,7 +926,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         if (i < nrows) {
           __builtin_amdgcn_wave_barrier();
           const int ph = (int)((uintptr_t)(done.rowp + (done.r0 + i) * done.rb) & 15);
-          const float sp = row_partial<FMT, 1>(sb, ph, lane, done.slice_n, xr);
+          const float sp = row_partial<FMT, C>(sb, ph, lane, done.slice_n, xr);
           acc[i] = wave_sum63(sp);
           __builtin_amdgcn_wave_barrier();
         }
@@ -1003,12 +1019,16 @@ int check_fmt_k(int32_t fmt, int64_t k) {
 
 // Team shape (WT waves, C block columns per lane) -- a function of k only.
 struct Shape { int wt, c; };
-// Team shape, a function of k only: one block column per lane while a row
-// fits 12 waves (k <= 24576), else two; the team has one wave per 64*C
-// columns, so every wave owns at least one block.
-int team_shape(int64_t k, Shape *s) {
+// Team shape, a function of (format, k) only.  Q8_0: one block column per
+// lane while a row fits 12 waves (k <= 24576), else two.  Q4_0 and MXFP4: two
+// columns per lane: their decode is VALU-bound, and a lane's second block
+// shares the row's staging, reduction and addressing work.  The team has
+// one wave per 64*C columns, so every wave owns at least one block.
+int first_c(int32_t fmt) { return fmt == QG_Q8_0 ? 1 : 2; }
+
+int team_shape(int32_t fmt, int64_t k, Shape *s) {
   const int64_t nb = k / 32;
-  for (int c = 1; c <= kMaxC; ++c) {
+  for (int c = first_c(fmt); c <= kMaxC; ++c) {
     const int64_t wt = (nb + 64 * c - 1) / (64 * c);
     if (wt <= kMaxWT) { s->wt = (int)wt; s->c = c; return QG_OK; }
   }
@@ -1029,7 +1049,7 @@ int check_matrix(const qg_matrix *w) {
   if (rc) return rc;
   if (w->n_rows < 0 || w->reserved != 0) return w->n_rows < 0 ? QG_E_SHAPE : QG_E_ARG;
   Shape s;
-  if ((rc = team_shape(w->k, &s))) return rc;
+  if ((rc = team_shape(w->fmt, w->k, &s))) return rc;
   if (w->n_bytes != w->n_rows * (w->k / 32) * block_bytes(w->fmt)) return QG_E_SIZE;
   if (!w->data && w->n_bytes > 0) return QG_E_NULL;
   if ((uintptr_t)w->data & 15) return QG_E_ARG;
@@ -1100,7 +1120,7 @@ int64_t count_tiles(const qg_window *win, int n, int64_t B, int tile_rows) {
 int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
                 hipStream_t stream) {
   Shape s;
-  int rc = team_shape(k, &s);
+  int rc = team_shape(fmt, k, &s);
   if (rc) return rc;
   qg_window win[kMaxWindows];
   int n = 0;
@@ -1160,7 +1180,7 @@ int validate_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win
   int rc = check_fmt_k(fmt, k);
   if (rc) return rc;
   Shape s;
-  if ((rc = team_shape(k, &s))) return rc;
+  if ((rc = team_shape(fmt, k, &s))) return rc;
   if (n_win < 0 || n_win > kMaxWindows || block_rows < 0) return QG_E_ARG;
   if (n_win > 0 && !win) return QG_E_NULL;
   for (int i = 0; i < n_win; ++i) {
@@ -1479,11 +1499,13 @@ namespace {
 
 typedef void (*ChainFn)(const ChainStepDev *, int, const ChainWinDev *, const int32_t *, ChainSync *, unsigned);
 
+// The chain uses the team shape of qgemv_rows at the same k (one column per
+// lane for Q8_0, two for Q4_0 and MXFP4), so its rows give the same bits.
 ChainFn chain_fn(int32_t fmt) {
   switch (fmt) {
-    case QG_Q8_0: return chain_kernel<QG_Q8_0>;
-    case QG_Q4_0: return chain_kernel<QG_Q4_0>;
-    default: return chain_kernel<QG_MXFP4>;
+    case QG_Q8_0: return chain_kernel<QG_Q8_0, 1>;
+    case QG_Q4_0: return chain_kernel<QG_Q4_0, 2>;
+    default: return chain_kernel<QG_MXFP4, 2>;
   }
 }
 
@@ -1536,7 +1558,8 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
   if (per_cu < 1) return hip_fail(hipErrorInvalidConfiguration, "chain workgroup does not fit a compute unit");
   const int grid = std::min(device_cus() * per_cu, kMaxChainGroups);
   const int bb = block_bytes(fmt);
-  const int cap = tile_cap(fmt, 1);
+  const int cc = first_c(fmt);  // block columns per lane (the chain takes k <= 24576: always this one)
+  const int cap = tile_cap(fmt, cc) - (cc == 2 ? 1 : 0);  // ChainRows
 
   std::vector<ChainWinDev> hw(n_win);
   for (int i = 0; i < n_win; ++i)
@@ -1546,7 +1569,7 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
   for (int s = 0; s < n_steps; ++s) {
     const qg_chain_step &S = steps[s];
     const int nb = (int)(S.k / 32);
-    const int wt = (nb + 63) / 64;
+    const int wt = (nb + 64 * cc - 1) / (64 * cc);
     const int tpw = kChainWaves / wt;
     const int64_t teams = (int64_t)grid * tpw;
     // Rows per tile: the fewest rows for the busiest team, with a small
