@@ -699,15 +699,16 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     ro.my_iters = member ? S.iters_q + (ro.tau < S.iters_r ? 1 : 0) : 0;
   };
 
+  // A tile, kept small (scalar registers are scarce in this kernel).
   struct Tile {
-    int s, w, j;              // step, window within the step, iteration within the step
-    int64_t r0, r1, row_start;
-    const QG_GLOBAL uint8_t *rowp;  // the window's row 0 advanced to this wave's slice
-    int64_t rb;
-    uint32_t slice_len;
-    int slice_n;
-    QG_GLOBAL float *y;
-    QG_GLOBAL float *act;
+    int s, w, j;                    // step, window within the step, iteration within the step
+    int nrows;                      // rows of the tile (at least 1)
+    uint32_t rb;                    // row bytes
+    uint32_t slice_len;             // bytes of the wave's slice of a row
+    int slice_n;                    // blocks of the wave's slice of a row
+    const QG_GLOBAL uint8_t *row0;  // the tile's first row advanced to the wave's slice
+    QG_GLOBAL float *y;             // y of the tile's first row
+    QG_GLOBAL float *act;           // act of the tile's first row, or null
   };
   auto locate = [&](const ChainStepDev &S, int s, int j, int t, int w_from, int wit, Tile &T) {
     int w = 0, tt = t;
@@ -718,18 +719,17 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
       tt = t - prefix[S.pre0 + w];
       W = load_win(wins + S.win0 + w);
     }
+    const int64_t off = (int64_t)tt * S.tile_rows;  // first row, from the window's start
     T.s = s;
     T.w = w;
     T.j = j;
-    T.row_start = W.row_start;
-    T.r0 = W.row_start + (int64_t)tt * S.tile_rows;
-    T.r1 = min(T.r0 + S.tile_rows, W.row_end);
+    T.nrows = (int)min((int64_t)S.tile_rows, W.row_end - W.row_start - off);
+    T.rb = (uint32_t)S.row_bytes;
     T.slice_n = min(SB, S.nb - SB * wit);
-    T.rowp = (const QG_GLOBAL uint8_t *)W.base + (int64_t)(SB * wit) * BB;
-    T.rb = S.row_bytes;
     T.slice_len = (uint32_t)(T.slice_n * BB);
-    T.y = (QG_GLOBAL float *)W.y;
-    T.act = (QG_GLOBAL float *)W.act;
+    T.row0 = (const QG_GLOBAL uint8_t *)W.base + (W.row_start + off) * S.row_bytes + (int64_t)(SB * wit) * BB;
+    T.y = (QG_GLOBAL float *)W.y + off;
+    T.act = W.act ? (QG_GLOBAL float *)W.act + off : nullptr;
   };
   // The tile after `cur`: the next one of its step, else the first tile of the
   // next step in which the wave's team has work.
@@ -752,7 +752,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
 
   u32x4 buf[R][V];
   auto fetch_row = [&](int i, const Tile &T) {
-    const QG_GLOBAL uint8_t *p = T.rowp + min(T.r0 + i, T.r1 - 1) * T.rb;
+    const QG_GLOBAL uint8_t *p = T.row0 + (uint32_t)min(i, T.nrows - 1) * T.rb;
     const uint32_t ph = (uint32_t)((uintptr_t)p & 15);
     const uint32_t last16 = ((ph + T.slice_len - 1) >> 4) << 4;
     const QG_GLOBAL uint8_t *pa = p - ph;
@@ -770,14 +770,14 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   float xr[C][32];
   auto gather_x = [&](const float *xg, int b0, int nb, float (&out)[32]) {
     const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg + 32 * min(b0, nb - 1);
-    const int nf = 32 * min(64, nb - b0);  // floats of x in the run (<= 0: none)
+    const int nbr = min(64, nb - b0);                  // blocks of the run (<= 0: none)
+    const uint32_t last = (uint32_t)max(32 * nbr, 4) - 4;  // last float quad inside x
+    // Unsigned offsets from a wave-uniform base (one offset register per
+    // load), and no per-load zeroing: a lane's block is past the row as a
+    // whole, so its inputs are zeroed after the turn-around instead.
     f32x4u t[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int off = 4 * (lane + 64 * q);
-      const f32x4u v = *(const QG_GLOBAL f32x4u *)(x + min(off, max(nf, 4) - 4));
-      t[q] = off < nf ? v : f32x4u{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    for (int q = 0; q < 8; ++q) t[q] = *(const QG_GLOBAL f32x4u *)(x + min(4u * (lane + 64 * q), last));
     uint8_t *sb = stage[wid][0];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -795,6 +795,10 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         }
       }
       __builtin_amdgcn_wave_barrier();
+    }
+    if (lane >= nbr) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) out[e] = 0.0f;
     }
   };
   // Per window (inside the tile loop, where the current tile's weights are
@@ -916,7 +920,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
         xw = cur.w;
       }
-      const int nrows = (int)(cur.r1 - cur.r0);
+      const int nrows = cur.nrows;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         uint8_t *sb = stage[wid][i & 1];
@@ -925,7 +929,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         if (now) fetch_row(i, nx);
         if (i < nrows) {
           __builtin_amdgcn_wave_barrier();
-          const int ph = (int)((uintptr_t)(done.rowp + (done.r0 + i) * done.rb) & 15);
+          const int ph = (int)((uintptr_t)(done.row0 + (uint32_t)i * done.rb) & 15);
           const float sp = row_partial<FMT, C>(sb, ph, lane, done.slice_n, xr);
           acc[i] = wave_sum63(sp);
           __builtin_amdgcn_wave_barrier();
@@ -937,12 +941,13 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
 #pragma unroll
           for (int i = 0; i < R; ++i)
             if (i < nrows) {
-              done.y[done.r0 + i - done.row_start] = acc[i];
-              if (done.act) done.act[done.r0 + i - done.row_start] = gelu_erf(acc[i]);
+              done.y[i] = acc[i];
+              if (done.act) done.act[i] = gelu_erf(acc[i]);
             }
         }
-      } else if (S.tpw == 1) {
-        // One team per workgroup: the hardware barrier is cheaper than the ring.
+      } else if (S.wt == kChainWaves) {
+        // The team is the whole workgroup: the hardware barrier is cheaper than
+        // the ring.  (Not with idle waves: they would not take these barriers.)
         if (lane == 63) {
 #pragma unroll
           for (int i = 0; i < R; ++i) red[j & 1][wid][i] = acc[i];
@@ -951,8 +956,8 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         if (wid == 0 && lane < nrows) {
           float sum = red[j & 1][0][lane];
           for (int v = 1; v < S.wt; ++v) sum += red[j & 1][v][lane];
-          done.y[done.r0 + lane - done.row_start] = sum;
-          if (done.act) done.act[done.r0 + lane - done.row_start] = gelu_erf(sum);
+          done.y[lane] = sum;
+          if (done.act) done.act[lane] = gelu_erf(sum);
         }
       } else {
         const int slot = j & (kRing - 1);
@@ -974,8 +979,8 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
           if (lane < nrows) {
             float sum = red[slot][ro.team0][lane];
             for (int v = 1; v < S.wt; ++v) sum += red[slot][ro.team0 + v][lane];
-            done.y[done.r0 + lane - done.row_start] = sum;
-            if (done.act) done.act[done.r0 + lane - done.row_start] = gelu_erf(sum);
+            done.y[lane] = sum;
+            if (done.act) done.act[lane] = gelu_erf(sum);
           }
           __builtin_amdgcn_wave_barrier();
           if (lane == 0) __hip_atomic_store(&consumed[tiw][slot], use + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);

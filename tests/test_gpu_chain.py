@@ -96,10 +96,12 @@ def teacher_forced(dense, s, y):
 
 
 @pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0, q.MXFP4])
-@pytest.mark.parametrize("H,F,L", [(3072, 8192, 2), (1024, 24576, 1)])
+@pytest.mark.parametrize("H,F,L", [(3072, 8192, 2), (1024, 24576, 1), (3072, 14336, 2)])
 def test_dense_chain_matches_separate_calls_and_oracle(dev, fmt, H, F, L):
     """Team shapes covered: k = 1024 (1 wave, 12 teams per workgroup), 3072
-    (2 waves), 8192 (4 waves), 24576 (12 waves, the whole workgroup)."""
+    (2 waves), 8192 (4 waves), 24576 (12 waves, the whole workgroup), and for
+    Q8_0 k = 14336 (one team of 7 waves, 5 idle: the step after it reads its
+    output with every wave busy)."""
     import torch
     d = Dense(dev, fmt, H, F, L, seed=7000 + 10 * fmt)
     with q.Chain(fmt, d.steps()) as ch:
