@@ -672,6 +672,10 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   __shared__ float red[kRing][kChainWaves][R];
   __shared__ unsigned arrived[kChainWaves][kRing], consumed[kChainWaves][kRing];
   __shared__ float ssq[kChainWaves * C];
+  // x of an RMS step with k <= kSharedX, read once by the whole workgroup.
+  constexpr int kSharedX = 8192;
+  constexpr int kSharedIt = (kSharedX / 4 + 64 * kChainWaves - 1) / (64 * kChainWaves);
+  __shared__ __attribute__((aligned(16))) float xsh[kSharedX];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -879,16 +883,58 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
       // Every window of an RMS step shares x: normalise it once for the step.
       // Column c of a lane's blocks is its own 64-block run, summed like one
       // wave of qgemv_rms_carry; the runs are then added in column order.
+      const bool gelu = S.in_op == QG_IN_GELU_RMS;
+      const bool shared = 32 * S.nb <= kSharedX;
+      if (shared) {
+        // Small x: the workgroup reads it once with contiguous loads (GELU
+        // applied on the way) instead of once per team, right after the
+        // barrier when every workgroup wants it.
+        const QG_GLOBAL f32x4u *xg = (const QG_GLOBAL f32x4u *)S.xs;
+        f32x4u v[kSharedIt];
+#pragma unroll
+        for (int it = 0; it < kSharedIt; ++it) {
+          const int f = (int)threadIdx.x + 64 * kChainWaves * it;
+          v[it] = xg[min(f, 8 * S.nb - 1)];
+        }
+#pragma unroll
+        for (int it = 0; it < kSharedIt; ++it) {
+          const int f = (int)threadIdx.x + 64 * kChainWaves * it;
+          if (f < 8 * S.nb) {
+            if (gelu) {
+              v[it].x = gelu_erf(v[it].x);
+              v[it].y = gelu_erf(v[it].y);
+              v[it].z = gelu_erf(v[it].z);
+              v[it].w = gelu_erf(v[it].w);
+            }
+            *(f32x4u *)&xsh[4 * f] = v[it];
+          }
+        }
+        __syncthreads();
+      }
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         float ss = 0.0f;
         if (busy) {
-          gather_x(S.xs, SB * ro.wit + 64 * c, S.nb, xr[c]);
+          if (shared) {
+            const int b = SB * ro.wit + 64 * c + lane;
+            const float *src = &xsh[32 * min(b, S.nb - 1)];
 #pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            if (S.in_op == QG_IN_GELU_RMS) xr[c][e] = gelu_erf(xr[c][e]);
-            ss = fmaf(xr[c][e], xr[c][e], ss);
+            for (int e = 0; e < 8; ++e) {
+              const f32x4u t = *(const f32x4u *)(src + 4 * e);
+              xr[c][4 * e + 0] = b < S.nb ? t.x : 0.0f;
+              xr[c][4 * e + 1] = b < S.nb ? t.y : 0.0f;
+              xr[c][4 * e + 2] = b < S.nb ? t.z : 0.0f;
+              xr[c][4 * e + 3] = b < S.nb ? t.w : 0.0f;
+            }
+          } else {
+            gather_x(S.xs, SB * ro.wit + 64 * c, S.nb, xr[c]);
+            if (gelu) {
+#pragma unroll
+              for (int e = 0; e < 32; ++e) xr[c][e] = gelu_erf(xr[c][e]);
+            }
           }
+#pragma unroll
+          for (int e = 0; e < 32; ++e) ss = fmaf(xr[c][e], xr[c][e], ss);
         }
         ss = wave_sum63(ss);
         if (lane == 63) ssq[C * wid + c] = ss;
