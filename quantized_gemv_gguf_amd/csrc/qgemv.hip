@@ -154,7 +154,7 @@ struct GemvArgs {
   int32_t tile_prefix[kMaxWindows + 1];  // tiles of windows [0, w)
   int64_t row_bytes;
   int64_t block_rows;  // > 0 (the host replaces 0 by a bound above every window)
-  int32_t n_win, nb, tile_rows, tiles_per_team, n_tiles;
+  int32_t n_win, nb, tile_rows, n_tiles;
 };
 
 // Sum over the 64 lanes of a wave in a fixed order (DPP row shifts, then row
@@ -204,8 +204,8 @@ __device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane
   return s;
 }
 
-// Largest rows per tile, per (format, block columns per lane): the fetched
-// rows of a tile live in registers until staged, sized to the register budget.
+// Largest rows per chain tile, per (format, block columns per lane): a chain
+// wave holds its tile's fetched rows in registers until staged.
 template <int FMT, int C> struct TileCap { static constexpr int value = 1; };
 template <> struct TileCap<QG_Q8_0, 1> { static constexpr int value = 6; };
 template <> struct TileCap<QG_Q8_0, 2> { static constexpr int value = 2; };
@@ -214,28 +214,56 @@ template <> struct TileCap<QG_Q4_0, 2> { static constexpr int value = 4; };
 template <> struct TileCap<QG_MXFP4, 1> { static constexpr int value = 8; };
 template <> struct TileCap<QG_MXFP4, 2> { static constexpr int value = 4; };
 
+// Weight staging of gemv_kernel: a wave's slice of a row is copied from HBM
+// straight into its LDS ring (gfx950 global_load_lds_dwordx4: lane l's 16
+// bytes land at M0 + 16 l), V loads per row, each a whole aligned 16-byte
+// granule per lane.  Lanes past the slice's last granule re-read that granule
+// into their own place beyond the data, so every load is unconditional and
+// the number of loads per row is a constant the waits can count.
+template <int FMT, int C> struct Geo {
+  static constexpr int CH = (15 + 64 * C * Fmt<FMT>::kBytes + 15) / 16;  // granules a slice can touch
+  static constexpr int V = (CH + 63) / 64;                               // loads per lane per row
+  static constexpr int SLOT = 1024 * V;                                  // ring slot bytes
+};
+
+// Concurrency of gemv_kernel, a function of the team size only: about six
+// waves per compute unit, each with NB rows in flight while it computes one
+// more.  More requests in flight than that (more waves, deeper rings) made
+// the same walk slower on MI355X: HBM serves a compact, moderate stream
+// better than a wide, deep one.
+__host__ __device__ constexpr int gemv_teams_per_cu(int wt) { return wt >= 6 ? 1 : 6 / wt; }
+__host__ __device__ constexpr int gemv_in_flight(int wt) { return wt * gemv_teams_per_cu(wt) <= 6 ? 2 : 1; }
+constexpr int kGemvTileRows = 8;  // most rows per tile
+
+// One asynchronous 16-byte HBM -> LDS copy per lane: global_load_lds_dwordx4
+// with a scalar base, a 32-bit lane offset and the LDS destination in M0.
+// Written as inline assembly because the compiler's own waits for LDS DMA
+// drain every outstanding load before any LDS read; here the kernel counts
+// its loads and waits with s_waitcnt vmcnt itself.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // One team = WT waves.  Wave w owns the contiguous block columns
 // [w*64*C, (w+1)*64*C) of every row (its "slice"), lane l the columns
 // w*64*C + l + 64*c, whose 32 activations each it keeps in registers.
-// A tile is up to R rows of one row block.  Each wave fetches the slice bytes
-// of a tile's rows with coalesced, 16-byte aligned loads into registers (row
-// i's chunks always in buf[i]); row by row it stages them in its own LDS
-// buffer, reissues buf[i] for row i of the next tile, and reads its blocks
-// back (dword reads realigned with v_alignbyte, any byte alignment).  So a
-// wave keeps about R rows of weights in flight at all times.  The team's
-// per-wave row sums meet in LDS and are added in wave order.
+// A tile is up to tile_rows rows of one row block; team b takes tiles
+// b, b + T, b + 2T, ... (T teams), so at any moment the grid works on a
+// compact band of the matrix.  Each wave streams its slices row after row
+// through an LDS ring of NB + 1 slots: before computing a row it issues the
+// copy of the row NB ahead (crossing tiles), so NB rows are in flight while
+// it decodes.  The team's per-wave row sums meet in LDS and are added in
+// wave order.
 template <int FMT, int WT, int C>
-__global__ void __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(3)))
-gemv_kernel(const GemvArgs a) {
-  using F = Fmt<FMT>;
-  constexpr int BB = F::kBytes;
-  constexpr int R = TileCap<FMT, C>::value;
-  constexpr int SB = 64 * C;                   // blocks per slice
-  constexpr int CH = (SB * BB + 15) / 16 + 1;  // 16-byte chunks a slice can touch
-  constexpr int V = (CH + 63) / 64;            // chunk loads per lane per row
-  constexpr int ROWB = 64 * V * 16 + 16;       // staged bytes per row, with read slack
-  __shared__ __attribute__((aligned(16))) uint8_t stage[WT][2][ROWB];
-  __shared__ float red[2][WT][R];
+__global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
+  using G = Geo<FMT, C>;
+  constexpr int V = G::V, SLOT = G::SLOT;
+  constexpr int NB = gemv_in_flight(WT), NS = NB + 1;
+  constexpr int SB = 64 * C;  // blocks per slice
+  __shared__ __attribute__((aligned(16))) uint8_t ring[WT][NS][SLOT];
+  __shared__ float red[2][WT][kGemvTileRows];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -243,57 +271,72 @@ gemv_kernel(const GemvArgs a) {
   const int64_t rb = a.row_bytes;
   const int slice_b0 = wave * SB;
   const int slice_n = max(0, min(SB, nb - slice_b0));  // >= 1 by the choice of WT
-  const int64_t slice_off = (int64_t)slice_b0 * BB;
-  const int slice_len = slice_n * BB;
+  const int64_t slice_off = (int64_t)slice_b0 * Fmt<FMT>::kBytes;
+  const uint32_t slice_len = (uint32_t)slice_n * Fmt<FMT>::kBytes;
+  const int T = gridDim.x;
+  if ((int)blockIdx.x >= a.n_tiles) return;
 
-  const int t_begin = blockIdx.x * a.tiles_per_team;
-  const int t_end = min(t_begin + a.tiles_per_team, a.n_tiles);
-  if (t_begin >= t_end) return;
-
-  // Kernel-argument fields used in the loop are read once into registers:
-  // a scalar reload inside the loop would wait on the LDS counter too.
+  // Kernel-argument fields used in the loop are read once into registers, and
+  // a window's fields again only when a cursor enters the next window.
   const int64_t B = a.block_rows;
   const int TR = a.tile_rows;
   const int tpb = (int)((B + TR - 1) / TR);
-  struct Tile {
-    int w;
-    int64_t r0, r1, row_start;
-    const uint8_t *base;
+  struct Win {
+    int w, t0, t1;  // window index, its tiles [t0, t1)
+    int64_t row_start, row_end;
+    const uint8_t *base;  // row 0, advanced to the wave's slice
     const float *x;
     float *y;
   };
-  auto locate = [&](int t, int w0, Tile &T) {
-    int w = w0;
-    while (t >= a.tile_prefix[w + 1]) ++w;
-    const int tt = t - a.tile_prefix[w];
-    const int blk = tt / tpb, tib = tt - blk * tpb;
-    T.w = w;
-    T.row_start = a.win[w].row_start;
-    T.base = a.win[w].base;
-    T.x = a.win[w].x;
-    T.y = a.win[w].y;
-    T.r0 = T.row_start + (int64_t)blk * B + (int64_t)tib * TR;
-    T.r1 = min(T.r0 + TR, min(T.row_start + (int64_t)(blk + 1) * B, a.win[w].row_end));
+  auto load_win = [&](int w, Win &W) {
+    W.w = w;
+    W.t0 = a.tile_prefix[w];
+    W.t1 = a.tile_prefix[w + 1];
+    W.row_start = a.win[w].row_start;
+    W.row_end = a.win[w].row_end;
+    W.base = a.win[w].base + slice_off;
+    W.x = a.win[w].x;
+    W.y = a.win[w].y;
+  };
+  struct Tile {
+    int t, nrows;
+    int64_t r0;
+  };
+  // Tile t of window W (advanced to the window holding t).
+  auto locate = [&](int t, Win &W, Tile &Q) {
+    if (t >= W.t1) {
+      int w = W.w + 1;
+      while (t >= a.tile_prefix[w + 1]) ++w;
+      load_win(w, W);
+    }
+    const int tt = t - W.t0;
+    // Row block and tile within it; a window of one row block (block_rows 0)
+    // needs no division.
+    int blk = 0, tib = tt;
+    if (tt >= tpb) {
+      blk = tt / tpb;
+      tib = tt - blk * tpb;
+    }
+    Q.t = t;
+    Q.r0 = W.row_start + (int64_t)blk * B + (int64_t)tib * TR;
+    const int64_t r1 = min(Q.r0 + TR, min(W.row_start + (int64_t)(blk + 1) * B, W.row_end));
+    Q.nrows = (int)(r1 - Q.r0);
   };
 
-  // Fetch row i of a tile (rows past the tile's end re-read its last row, and
-  // chunks past the slice re-read its last chunk: every load stays in bounds
-  // and is unconditional, so the compiler can count them exactly).
-  u32x4 buf[R][V];
-  // The row address, its phase and the last chunk are wave-uniform (scalar);
-  // a lane adds only its 32-bit chunk offset.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
   const uint32_t lane16 = 16u * lane;
-  auto fetch_row = [&](int i, const Tile &T) {
-    const uint8_t *p = T.base + slice_off + min(T.r0 + i, T.r1 - 1) * rb;
+  // Copy the wave's slice of row r0 + i of tile Q (window W) into ring slot s.
+  auto issue = [&](const Win &W, const Tile &Q, int i, int s) {
+    const uint8_t *p = W.base + (Q.r0 + i) * rb;
     const uint32_t ph = (uint32_t)((uintptr_t)p & 15);
-    const uint32_t last16 = ((ph + (uint32_t)slice_len - 1) >> 4) << 4;
+    const uint32_t last16 = ((ph + slice_len - 1) >> 4) << 4;
     const uint8_t *pa = p - ph;
+    const uint32_t l = lds0 + SLOT * s;
 #pragma unroll
-    for (int v = 0; v < V; ++v) buf[i][v] = *(const u32x4 *)(pa + min(lane16 + 1024u * v, last16));
+    for (int v = 0; v < V; ++v) dma16(pa, min(lane16 + 1024u * v, last16), l + 1024u * v);
   };
 
   float xr[C][32];
-  int xw = -1;
   auto load_x = [&](const float *x) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -312,65 +355,83 @@ gemv_kernel(const GemvArgs a) {
     }
   };
 
-  int t = t_begin;
-  Tile cur, nxt;
-  locate(t, 0, cur);
+  // Fetch cursor: the next row to copy (tile F of window FW, row fi).  Past
+  // the team's last row it re-copies that row into a slot no computation
+  // reads, which keeps one fixed count of loads per row.
+  Win CW, FW;
+  load_win(0, CW);
+  Tile cur, F;
+  locate(blockIdx.x, CW, cur);
+  FW = CW;
+  F = cur;
+  int fi = 0;
+  bool f_end = false;
+  auto advance_fetch = [&]() {
+    if (f_end) return;
+    if (fi + 1 < F.nrows) { ++fi; return; }
+    if (F.t + T < a.n_tiles) { locate(F.t + T, FW, F); fi = 0; }
+    else f_end = true;
+  };
+  load_x(CW.x);  // before the ring's first copies: its wait then drains nothing else
 #pragma unroll
-  for (int i = 0; i < R; ++i) fetch_row(i, cur);
+  for (int s = 0; s < NB; ++s) {
+    issue(FW, F, fi, s);
+    advance_fetch();
+  }
+  int xw = CW.w;
+  int slot = 0;  // ring slot of the row being computed
   int parity = 0;
   for (;;) {
-    const bool more = t + 1 < t_end;
-    nxt = cur;
-    if (more) locate(t + 1, cur.w, nxt);
-    if (cur.w != xw) {
-      load_x(cur.x);
-      xw = cur.w;
+    if (CW.w != xw) {
+      load_x(CW.x);
+      xw = CW.w;
     }
-    const int nrows = (int)(cur.r1 - cur.r0);
-    float acc[R];
+    const int nrows = cur.nrows;
+    float acc[kGemvTileRows];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
+    for (int i = 0; i < kGemvTileRows; ++i) {
       acc[i] = 0.0f;
-      // Stage row i (unconditionally: a row past the tile's end writes a
-      // buffer no later read uses), then reuse buf[i] for the next tile.
-      uint8_t *sb = stage[wave][i & 1];
-#pragma unroll
-      for (int v = 0; v < V; ++v) *(u32x4 *)(sb + lane16 + 1024 * v) = buf[i][v];
-      if (more) fetch_row(i, nxt);
       if (i < nrows) {
-        // Other lanes' staged bytes are read below: keep the order (LDS
-        // operations of one wave complete in order).
-        __builtin_amdgcn_wave_barrier();
-        const int ph = (int)((uintptr_t)(cur.base + slice_off + (cur.r0 + i) * rb) & 15);
-        const float s = row_partial<FMT, C>(sb, ph, lane, slice_n, xr);
-        acc[i] = wave_sum63(s);
-        __builtin_amdgcn_wave_barrier();
+        // The slot NB ahead held the previous row, whose LDS reads are done.
+        int s2 = slot + NB;
+        s2 = s2 >= NS ? s2 - NS : s2;
+        wait_lds_reads();
+        issue(FW, F, fi, s2);
+        advance_fetch();
+        wait_vmcnt<V * NB>();  // this row's copies have landed
+        const uint8_t *sb = &ring[wave][slot][0];
+        const int ph = (int)((uintptr_t)(CW.base + (cur.r0 + i) * rb) & 15);
+        acc[i] = wave_sum63(row_partial<FMT, C>(sb, ph, lane, slice_n, xr));
+        slot = slot + 1 == NS ? 0 : slot + 1;
       }
     }
+    float *yt = CW.y + (cur.r0 - CW.row_start);
     if (WT == 1) {
       if (lane == 63) {
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-          if (i < nrows) cur.y[cur.r0 + i - cur.row_start] = acc[i];
+        for (int i = 0; i < kGemvTileRows; ++i)
+          if (i < nrows) yt[i] = acc[i];
       }
     } else {
       if (lane == 63) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) red[parity][wave][i] = acc[i];
+        for (int i = 0; i < kGemvTileRows; ++i) red[parity][wave][i] = acc[i];
       }
       __syncthreads();
       if ((int)threadIdx.x < nrows) {
         float s = red[parity][0][threadIdx.x];
 #pragma unroll
         for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
-        cur.y[cur.r0 + threadIdx.x - cur.row_start] = s;
+        yt[threadIdx.x] = s;
       }
       parity ^= 1;
     }
-    if (!more) break;
-    ++t;
-    cur = nxt;
+    if (cur.t + T >= a.n_tiles) break;
+    locate(cur.t + T, CW, cur);
   }
+  // The ring's last copies (re-reads past the end) must land before the
+  // workgroup's LDS is released.
+  wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -1149,25 +1210,13 @@ GemvFn pick(int32_t fmt, Shape s) {
   }
 }
 
-// Tiles of n windows with tile_rows rows each, never across a row block of B.
-int64_t count_tiles(const qg_window *win, int n, int64_t B, int tile_rows) {
-  int64_t tiles = 0;
-  const int64_t tpb = (B + tile_rows - 1) / tile_rows;
-  for (int i = 0; i < n; ++i) {
-    const int64_t len = win[i].row_end - win[i].row_start;
-    const int64_t full = len / B, rem = len - full * B;
-    tiles += full * tpb + (rem + tile_rows - 1) / tile_rows;
-  }
-  return tiles;
-}
-
 // Launch one grid over n windows (already validated).  win[i].data is the
 // device address of the window's matrix row 0.
 //
 // Work split (it never changes a row's result): the grid has at most
-// CUs * 12 / WT teams (3 waves per SIMD); tiles hold tile_rows <= R rows, and
-// tile_rows is picked to minimise the rows the busiest team walks, with a
-// small charge per tile.
+// CUs * gemv_teams_per_cu(WT) teams, team b taking tiles b, b + T, ...; tiles
+// hold up to kGemvTileRows rows, fewer when the rows are too few to give every
+// team a tile, and never cross a row block.
 int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
                 hipStream_t stream) {
   Shape s;
@@ -1175,26 +1224,18 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   if (rc) return rc;
   qg_window win[kMaxWindows];
   int n = 0;
-  int64_t maxlen = 1;
+  int64_t maxlen = 1, total = 0;
   for (int i = 0; i < n_in; ++i) {
     if (win_in[i].row_end == win_in[i].row_start) continue;
     win[n++] = win_in[i];
     maxlen = std::max<int64_t>(maxlen, win_in[i].row_end - win_in[i].row_start);
+    total += win_in[i].row_end - win_in[i].row_start;
   }
   if (n == 0) return QG_OK;
   const int64_t B = block_rows > 0 ? std::min<int64_t>(block_rows, maxlen) : maxlen;
-  const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * 12 / s.wt);
-  const int cap = tile_cap(fmt, s.c);
-  int best_tr = 1;
-  double best_cost = 1e300;
-  for (int tr = 1; tr <= cap; ++tr) {
-    const int64_t tiles = count_tiles(win, n, B, tr);
-    const int64_t teams = std::min(teams_max, tiles);
-    const int64_t tpt = (tiles + teams - 1) / teams;
-    const double cost = (double)tpt * tr + 0.5 * (double)tpt;
-    if (cost < best_cost - 1e-9) { best_cost = cost; best_tr = tr; }
-  }
-  const int tile_rows = best_tr;
+  const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * gemv_teams_per_cu(s.wt));
+  const int tile_rows =
+      (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kGemvTileRows, B, (total + teams_max - 1) / teams_max}));
   GemvArgs a;
   memset(&a, 0, sizeof(a));
   int64_t tiles = 0;
@@ -1218,10 +1259,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   a.block_rows = B;
   a.tile_rows = tile_rows;
   a.n_tiles = (int32_t)tiles;
-  int64_t teams = std::min<int64_t>(teams_max, tiles);
-  const int64_t tpt = (tiles + teams - 1) / teams;
-  teams = (tiles + tpt - 1) / tpt;
-  a.tiles_per_team = (int32_t)tpt;
+  const int64_t teams = std::min<int64_t>(teams_max, tiles);
   hipLaunchKernelGGL(pick(fmt, s), dim3((unsigned)teams), dim3(64 * s.wt), 0, stream, a);
   QG_HIP(hipGetLastError());
   return QG_OK;
