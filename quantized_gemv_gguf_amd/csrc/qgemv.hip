@@ -226,13 +226,19 @@ template <int FMT, int C> struct Geo {
   static constexpr int SLOT = 1024 * V;                                  // ring slot bytes
 };
 
-// Concurrency of gemv_kernel, a function of the team size only: about six
-// waves per compute unit, each with NB rows in flight while it computes one
-// more.  More requests in flight than that (more waves, deeper rings) made
-// the same walk slower on MI355X: HBM serves a compact, moderate stream
-// better than a wide, deep one.
-__host__ __device__ constexpr int gemv_teams_per_cu(int wt) { return wt >= 6 ? 1 : 6 / wt; }
-__host__ __device__ constexpr int gemv_in_flight(int wt) { return wt * gemv_teams_per_cu(wt) <= 6 ? 2 : 1; }
+// Concurrency of gemv_kernel, a function of (format, team size): Q8_0 runs
+// about six waves per compute unit, each with two rows in flight while it
+// computes one more; the 4-bit formats, with twice the decode work per byte,
+// run twelve waves with one row in flight.  More requests in flight than that
+// (more waves, deeper rings) made the same walks slower on MI355X: HBM serves
+// a compact, moderate stream better than a wide, deep one.
+__host__ __device__ constexpr int gemv_waves_per_cu(int fmt) { return fmt == QG_Q8_0 ? 6 : 12; }
+__host__ __device__ constexpr int gemv_teams_per_cu(int fmt, int wt) {
+  return wt >= gemv_waves_per_cu(fmt) ? 1 : gemv_waves_per_cu(fmt) / wt;
+}
+__host__ __device__ constexpr int gemv_in_flight(int fmt, int wt) {
+  return fmt == QG_Q8_0 && wt * gemv_teams_per_cu(fmt, wt) <= 6 ? 2 : 1;
+}
 constexpr int kGemvTileRows = 8;  // most rows per tile
 
 // One asynchronous 16-byte HBM -> LDS copy per lane: global_load_lds_dwordx4
@@ -260,7 +266,7 @@ template <int FMT, int WT, int C>
 __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   using G = Geo<FMT, C>;
   constexpr int V = G::V, SLOT = G::SLOT;
-  constexpr int NB = gemv_in_flight(WT), NS = NB + 1;
+  constexpr int NB = gemv_in_flight(FMT, WT), NS = NB + 1;
   constexpr int SB = 64 * C;  // blocks per slice
   __shared__ __attribute__((aligned(16))) uint8_t ring[WT][NS][SLOT];
   __shared__ float red[2][WT][kGemvTileRows];
@@ -1214,7 +1220,7 @@ GemvFn pick(int32_t fmt, Shape s) {
 // device address of the window's matrix row 0.
 //
 // Work split (it never changes a row's result): the grid has at most
-// CUs * gemv_teams_per_cu(WT) teams, team b taking tiles b, b + T, ...; tiles
+// CUs * gemv_teams_per_cu(fmt, WT) teams, team b taking tiles b, b + T, ...; tiles
 // hold up to kGemvTileRows rows, fewer when the rows are too few to give every
 // team a tile, and never cross a row block.
 int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
@@ -1233,7 +1239,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   }
   if (n == 0) return QG_OK;
   const int64_t B = block_rows > 0 ? std::min<int64_t>(block_rows, maxlen) : maxlen;
-  const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * gemv_teams_per_cu(s.wt));
+  const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * gemv_teams_per_cu(fmt, s.wt));
   const int tile_rows =
       (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kGemvTileRows, B, (total + teams_max - 1) / teams_max}));
   GemvArgs a;
