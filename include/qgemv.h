@@ -200,6 +200,22 @@ int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_windo
 /* Waits for the streamer's work, frees it.  NULL is a no-op. */
 int qgemv_stream_destroy(qg_streamer *st);
 
+/* ---- host-mapped weights (zero copy) ----
+ * The weights stay in page-locked host memory (hipHostMalloc, mapped into the
+ * device's address space) and the same kernels read them in place over the
+ * host link: no device copy, no ring, no copy stream (hipfire PR, "Design
+ * notes": host memory from hipHostMalloc with hipHostMallocMapped, kernels
+ * unchanged, dereferencing the host-mapped alias; its "pcie" execution arm).
+ * Every other argument, the validation and the result are those of
+ * qgemv_rows / qgemv_windows, so a row gives the same bits resident, streamed
+ * or mapped.  Weights not in page-locked host memory (pageable or device
+ * memory) give QG_E_NOT_PINNED before anything is enqueued.  The host memory
+ * must stay allocated and unmodified until the work on `stream` has finished. */
+int qgemv_mapped_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, float *y,
+                      int64_t block_rows, qg_stream_t stream);
+int qgemv_mapped_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win,
+                         int64_t block_rows, qg_stream_t stream);
+
 /* ---- chains: dependent GEMVs in one persistent grid ----
  * A decode pass is a sequence of GEMVs, each taking the previous one's output
  * through a small transform.  Launched one by one, every GEMV ends with a

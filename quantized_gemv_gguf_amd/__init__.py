@@ -90,6 +90,8 @@ def lib():
         "qgemv_stream_rows": ([_vp, P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
         "qgemv_stream_windows": ([_vp, _i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_stream_destroy": ([_vp], ctypes.c_int),
+        "qgemv_mapped_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
+        "qgemv_mapped_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_chain_create": ([_i32, P(qg_chain_step), _i32, P(qg_chain_window), _i32, P(_vp)], ctypes.c_int),
         "qgemv_chain_run": ([_vp, _vp], ctypes.c_int),
         "qgemv_chain_check": ([_vp], ctypes.c_int),
@@ -218,6 +220,24 @@ def qgemv_expert_windows(mats: Sequence[Matrix], n_expert: int, ids, x, x_stride
     yp = _f32(y, len(mats) * len(ids) * out, "y")
     _check(lib().qgemv_expert_windows(marr, len(mats), n_expert, iarr, len(ids), xp, x_stride, yp,
                                       block_rows, _stream(stream)), "qgemv_expert_windows")
+
+
+def qgemv_mapped_rows(w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 0,
+                      stream=None) -> None:
+    """As qgemv_rows, with ``w.data`` a pinned host tensor read in place over the host link."""
+    m = w.c()
+    n = max(row_end - row_start, 0)
+    _check(lib().qgemv_mapped_rows(ctypes.byref(m), row_start, row_end, _f32(x, w.k, "x"), _f32(y, n, "y"),
+                                   block_rows, _stream(stream)), "qgemv_mapped_rows")
+
+
+def qgemv_mapped_windows(windows: Sequence[Window], block_rows: int = 0, stream=None, fmt=None, k=None) -> None:
+    """As qgemv_windows, with every window's matrix in pinned host memory."""
+    arr, n, f, kk = _windows(windows)
+    f = fmt if f is None else f
+    kk = k if kk is None else kk
+    _check(lib().qgemv_mapped_windows(int(f or Q8_0), int(kk or 32), arr, n, block_rows, _stream(stream)),
+           "qgemv_mapped_windows")
 
 
 def qgemv_silu_mul(g, u, h, stream=None) -> None:

@@ -1513,6 +1513,23 @@ int check_pinned(const void *p) {
   return QG_OK;
 }
 
+// The device address of page-locked host memory (hipHostMalloc; mapped into
+// every device's address space), or QG_E_NOT_PINNED for pageable or device
+// memory.  Checked before anything is enqueued.
+int mapped_alias(const void *host, const void **dev) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, host);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return QG_E_NOT_PINNED;
+  }
+  if (attr.type != hipMemoryTypeHost || !attr.devicePointer) return QG_E_NOT_PINNED;
+  if ((uintptr_t)attr.devicePointer & 15) return QG_E_ARG;
+  *dev = attr.devicePointer;
+  return QG_OK;
+}
+
 // Stream the row blocks of validated windows through the ring.
 int stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win, int n_win,
                    int64_t block_rows, hipStream_t stream) {
@@ -1571,6 +1588,36 @@ int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_windo
   if (rc) return rc;
   if (n_win == 0) return QG_OK;
   return stream_windows(st, fmt, k, win, n_win, block_rows, stream);
+}
+
+// ---- host-mapped weights: the kernels read page-locked host memory in place ----
+
+int qgemv_mapped_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, float *y,
+                      int64_t block_rows, qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  if (block_rows < 0) return QG_E_ARG;
+  if (row_end == row_start) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  const void *dev = nullptr;
+  if ((rc = mapped_alias(w->data, &dev))) return rc;
+  qg_window win = {dev, w->n_rows, row_start, row_end, x, y};
+  return launch_gemv(w->fmt, w->k, &win, 1, block_rows, stream);
+}
+
+int qgemv_mapped_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win, int64_t block_rows,
+                         qg_stream_t stream) {
+  int rc = validate_windows(fmt, k, win, n_win, block_rows);
+  if (rc) return rc;
+  if (n_win == 0) return QG_OK;
+  qg_window dw[kMaxWindows];
+  for (int i = 0; i < n_win; ++i) {
+    dw[i] = win[i];
+    if (win[i].row_end == win[i].row_start) continue;
+    if ((rc = mapped_alias(win[i].data, &dw[i].data))) return rc;
+  }
+  return launch_gemv(fmt, k, dw, n_win, block_rows, stream);
 }
 
 }  // extern "C"

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -181,6 +181,28 @@ def test_streamer_validation():
     assert L.qgemv_stream_destroy(None) == 0
     assert L.qgemv_stream_rows(None, ctypes.byref(mat()), 0, 8, 0, FAKE, FAKE, None) == E_NULL
     assert L.qgemv_stream_windows(None, 1, 64, None, 0, 0, None) == E_NULL
+
+
+def test_mapped_validation():
+    # argument checks precede the page-locked check (which needs the runtime)
+    L = q.lib()
+
+    def call(m, r0=0, r1=8, x=FAKE, y=FAKE, B=0):
+        return L.qgemv_mapped_rows(ctypes.byref(m) if m is not None else None, r0, r1, x, y, B, None)
+
+    assert call(None) == E_NULL
+    assert call(mat(fmt=5)) == E_FMT
+    assert call(mat(k=48, nbytes=0)) == E_SHAPE
+    assert call(mat(data=FAKE + 4)) == E_ARG
+    assert call(mat(nbytes=8 * 2 * 34 - 1)) == E_SIZE
+    assert call(mat(), r1=9) == E_RANGE
+    assert call(mat(), B=-1) == E_ARG
+    assert call(mat(), x=0) == E_NULL
+    assert call(mat(), r0=2, r1=2, x=0, y=0) == 0
+    assert L.qgemv_mapped_windows(1, 64, None, 1, 0, None) == E_NULL
+    assert L.qgemv_mapped_windows(1, 64, None, 0, 0, None) == 0
+    assert L.qgemv_mapped_windows(1, 48, None, 0, 0, None) == E_SHAPE
+    assert L.qgemv_mapped_windows(1, 64, None, 65, 0, None) == E_ARG
 
 
 def test_strerror_and_version():
