@@ -6,7 +6,10 @@ out 6144x6144, up 24576x6144, down 6144x24576; 21.18 GB resident in HBM).  A
 step is one token: the 176 GEMVs of the pass, in order, each fed by the RMS
 carry of the previous one (the attention over a single position returns V, so
 the carry after QKV is the RMS-normalised V third).  Weights are random-init
-synthetic blocks; nothing is cached or skipped between tokens.
+synthetic blocks; nothing is cached or skipped between tokens.  Each GEMV is
+one qgemv_rows_op launch that normalises its raw input as it loads it (the
+up projection stores gelu(u)); --chain runs the pass as one persistent
+chain launch per token instead.
 
 Printed: one JSON line with the headline metric (effective weight GB/s of the
 whole timed region = weight bytes read / wall time), the roofline of the
@@ -125,6 +128,16 @@ class DensePass:
                                    self.w[l][m].numel(), k, m))
         self.v_ptr = self.qkv.data_ptr() + 4 * 2 * hidden  # the V third of QKV
         self.bytes_per_token = sum(c[4] for c in self.calls)
+        # fused launches (qgemv_rows_op): each GEMV normalises its raw input as it
+        # loads it; the up projection stores gelu(u).  d carries from token to token.
+        fin = [self.d.data_ptr(), self.v_ptr, self.o.data_ptr(), self.a.data_ptr()]
+        fout = [self.qkv, self.o, self.a, self.d]
+        self.fcalls = []
+        for l in range(layers):
+            for m, (_, r, k) in enumerate(self.shapes):
+                mp, _, _, _, nbytes, _, _ = self.calls[4 * l + m]
+                self.fcalls.append((mp, r, fin[m], fout[m].data_ptr(), nbytes, k, m,
+                                    q.OUT_GELU if m == 2 else q.OUT_Y))
 
     @staticmethod
     def seed(layer, m):
@@ -172,6 +185,25 @@ class DensePass:
         rc = self.lib.qgemv_rms_carry(self.x0.data_ptr(), self.c.data_ptr(), self.H, self.eps, 0, self.stream)
         assert rc == 0
 
+    def reset_fused(self):
+        self.d.copy_(self.x0)
+
+    def token_fused(self, events=None, hook=None, stream=None):
+        """One token as 176 fused GEMV launches (qgemv_rows_op).  events: one
+        (start, end) pair per GEMV, recorded around it on the launch stream."""
+        L, q = self.lib, self.q
+        st = self.stream if stream is None else stream
+        for i, (mp, r, xp, yp, nbytes, k, m, out_op) in enumerate(self.fcalls):
+            if events is not None:
+                events[i][0].record()
+            rc = L.qgemv_rows_op(mp, 0, r, xp, None, q.IN_RMS, self.eps, out_op, yp, 0, st)
+            if events is not None:
+                events[i][1].record()
+            if rc != 0:
+                raise RuntimeError(f"qgemv_rows_op failed: {rc}")
+            if hook is not None:
+                hook(i, m)
+
     def token(self, events=None, hook=None):
         """One token's pass.  events: list of (start, end) torch events, one
         pair per GEMV, recorded around it on the launch stream."""
@@ -200,30 +232,54 @@ def dense_workload(args, dev):
     c = synth.CONFIGS[5]
     layers = args.layers or c["layers"]
     model = DensePass(layers, c["hidden"], c["ffn"], dev)
-    if not args.separate:
+    if args.chain:
         return dense_chain_workload(args, dev, model, c, layers)
     torch.cuda.synchronize()
-    model.reset()
+    model.reset_fused()
     for _ in range(args.warmup):
-        model.token()
+        model.token_fused()
     torch.cuda.synchronize()
-    n = len(model.calls)
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-              for _ in range(args.steps)]
+    n = len(model.fcalls)
+    graph = None
+    if args.graph:
+        # one token's 176 launches captured once, replayed per token
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            model.token_fused(stream=cap.cuda_stream)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            model.token_fused(stream=cap.cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record()
     for s in range(args.steps):
-        model.token(events[s])
+        if graph is not None:
+            graph.replay()
+        else:
+            model.token_fused()
     g1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = g0.elapsed_time(g1)
-    # per-launch durations, grouped by kernel variant (k decides the variant)
+    # per-launch durations (HIP events around every launch on its stream), from
+    # eager tokens after the timed region, grouped by kernel variant (k decides it)
+    n_ev = max(2, min(args.steps, 8))
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+              for _ in range(n_ev)]
+    for s in range(n_ev):
+        model.token_fused(events[s])
+    torch.cuda.synchronize()
     per_k = {}
-    for s in range(args.steps):
-        for i, (mp, r, xp, yp, nbytes, k, m) in enumerate(model.calls):
+    for s in range(n_ev):
+        for i, (mp, r, xp, yp, nbytes, k, m, _) in enumerate(model.fcalls):
             ms = events[s][i][0].elapsed_time(events[s][i][1])
             e = per_k.setdefault(k, [0, 0.0, 0])
             e[0] += nbytes
@@ -247,7 +303,9 @@ def dense_workload(args, dev):
         "bytes_per_token": model.bytes_per_token,
         "config": {"workload": c["name"], "layers": layers, "hidden": c["hidden"], "ffn": c["ffn"],
                    "format": "Q8_0", "tokens": args.steps, "gemvs_per_token": n,
-                   "weight_bytes_per_token": model.bytes_per_token},
+                   "weight_bytes_per_token": model.bytes_per_token,
+                   "launch": "176 fused GEMV launches per token (RMS carry in the x-load, GELU in the store)"
+                             + (", one HIP graph per token" if graph is not None else "")},
         "roofline": {"bound": "hbm", "kernel": f"gemv_q8_0_k{dom_k}", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic(f"gemv_q8_0_k{dom_k}"), "avg_launch_us": ms / cnt * 1e3,
@@ -357,30 +415,53 @@ def dense_parity(model, layers, n_rows=48, seed=7):
     import oracle
     rng = np.random.default_rng(seed)
     want = {0, 1, 2, 3, 4 * (layers - 1), 4 * (layers - 1) + 1, 4 * (layers - 1) + 2, 4 * (layers - 1) + 3}
-    ins = [model.c, model.c, model.c, model.a]
-    outs = [model.qkv, model.o, model.u, model.d]
+    # fused launches: GEMV i normalises its raw input (oracle: fp64 RMS of
+    # the GPU's own input) and the up projection stores gelu(u)
+    outs = [model.qkv, model.o, model.a, model.d]
     worst_n, worst_c = 0.0, 0.0
     checked = 0
+    H = model.H
+    state = {}
+
+    def raw_input(i, m):
+        if m == 0:
+            return state["d_in"]
+        if m == 1:
+            return model.qkv[2 * H:3 * H].cpu().numpy()
+        return (model.o if m == 2 else model.a).cpu().numpy()
 
     def hook(i, m):
         nonlocal worst_n, worst_c, checked
         if i not in want:
+            if m == 3:
+                torch.cuda.synchronize()
+                state["d_in"] = model.d.cpu().numpy()
             return
         torch.cuda.synchronize()
-        x = ins[m].cpu().numpy()
+        x = oracle.rms_carry(raw_input(i, m).astype(np.float64), model.eps, gelu=False)
         y = outs[m].cpu().numpy().astype(np.float64)
+        if m == 3:
+            state["d_in"] = model.d.cpu().numpy()
         _, r, k = model.shapes[m]
         rows = np.sort(rng.choice(r, n_rows, replace=False))
         ref, a = np.empty(n_rows), np.empty(n_rows)
         for j, row in enumerate(rows):
             wrow = synth.blocks(synth.Q8_0, r, k, model.seed(i // 4, m), r0=int(row), r1=int(row) + 1, threads=1)
             ref[j], a[j] = [v[0] for v in oracle.gemv_rows(oracle.Q8_0, wrow, 1, k, x, threads=1)]
+        if m == 2:  # the stored output is gelu(u): compare u's GELU in fp64
+            from math import erfc, sqrt
+            ref = np.array([0.5 * v * erfc(-v / sqrt(2.0)) for v in ref])
+            # |gelu'| <= 1.13 carries u's error through; the fp32 erfc adds a
+            # rounding error relative to |gelu(u)|
+            a = 1.13 * a + np.abs(ref)
         err = np.abs(y[rows] - ref)
         worst_c = max(worst_c, float(np.max(err / a)))
         worst_n = max(worst_n, float(err.max() / np.abs(ref).max()))
         checked += n_rows
 
-    model.token(hook=hook)
+    torch.cuda.synchronize()
+    state["d_in"] = model.d.cpu().numpy()
+    model.token_fused(hook=hook)
     torch.cuda.synchronize()
     ok = worst_c <= TOL and worst_n <= TOL
     return {"rows_checked": checked, "max_componentwise": worst_c, "max_normwise_sampled": worst_n,
@@ -674,8 +755,10 @@ def main(argv=None):
     p.add_argument("--workload", default="dense20b",
                    choices=sorted(WORKLOADS))
     p.add_argument("--layers", type=int, default=0, help="fewer layers for a quick run (not a valid headline)")
-    p.add_argument("--separate", action="store_true",
-                   help="dense pass as separate launches (GEMV, then carry) instead of one chain per token")
+    p.add_argument("--chain", action="store_true",
+                   help="dense pass as one chain launch per token (qgemv_chain_run) instead of 176 fused GEMV launches")
+    p.add_argument("--graph", action="store_true", help="replay one token's 176 fused launches as a HIP graph")
+    p.add_argument("--separate", action="store_true", help="the default: 176 fused GEMV launches per token")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -128,6 +128,33 @@ int64_t qgemv_weight_bytes(int32_t fmt, int64_t n_rows, int64_t k);
 int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
                const float *x, float *y, int64_t block_rows, qg_stream_t stream);
 
+/* Input transforms (qgemv_rows_op, chain steps) and output transforms
+ * (qgemv_rows_op). */
+enum qg_in_op { QG_IN_X = 0, QG_IN_RMS = 1, QG_IN_GELU_RMS = 2, QG_IN_SILU_MUL = 3 };
+enum qg_out_op { QG_OUT_Y = 0, QG_OUT_GELU = 1 };
+
+/* As qgemv_rows, with the activation transformed as it is loaded and each
+ * output as it is stored, so that a decode pass needs no elementwise launch
+ * between its GEMVs (neurostream README, "What the numbers taught us": the
+ * time per step went to drains and small launches, not to bytes):
+ *   in_op  QG_IN_X         x
+ *          QG_IN_RMS       rms(x) = x / sqrt(mean(x^2) + eps), as
+ *                          qgemv_rms_carry(gelu = 0); k <= 32768
+ *          QG_IN_SILU_MUL  silu(x) * x2 elementwise, as qgemv_silu_mul
+ *   out_op QG_OUT_Y        y = W x'
+ *          QG_OUT_GELU     y = gelu(W x'), the exact (erf) GELU, once per row
+ * (QG_IN_GELU_RMS is not an input op here: store the producer's output with
+ * QG_OUT_GELU and normalise it with QG_IN_RMS.)  Each transform is computed
+ * in the order the separate calls use, so the result has their bits: e.g.
+ * qgemv_rows_op(..., QG_IN_RMS, eps, QG_OUT_Y, y) equals qgemv_rms_carry(x,
+ * t, eps, 0) followed by qgemv_rows(t -> y), and GELU-stored y normalised by
+ * QG_IN_RMS equals qgemv_rms_carry(y, t, eps, 1).  x2: device, k values,
+ * required for QG_IN_SILU_MUL only.  Errors: an unknown op, eps < 0 or not
+ * finite, or k > 32768 with QG_IN_RMS give QG_E_ARG; otherwise as qgemv_rows. */
+int qgemv_rows_op(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x,
+                  const float *x2, int32_t in_op, float eps, int32_t out_op, float *y,
+                  int64_t block_rows, qg_stream_t stream);
+
 /* Several row windows (any matrices of the same fmt and k, each with its own
  * x and y) computed by ONE grid.  win is a host array of n_win entries,
  * 0 <= n_win <= QG_MAX_WINDOWS; n_win = 0 is a no-op. */
@@ -237,7 +264,7 @@ int qgemv_mapped_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n
  * computed in qgemv_rows' per-row order and each transform in the order of
  * the call named beside it, so a chain gives the same bits as the equivalent
  * sequence of separate calls. */
-enum qg_in_op { QG_IN_X = 0, QG_IN_RMS = 1, QG_IN_GELU_RMS = 2, QG_IN_SILU_MUL = 3 };
+/* (enum qg_in_op is declared with qgemv_rows_op above.) */
 
 typedef struct qg_chain_window {
   const void *data;  /* the matrix's row 0, device, 16-byte aligned */

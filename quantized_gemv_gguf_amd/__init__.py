@@ -20,6 +20,7 @@ MAX_WINDOWS = 64
 MAX_K = 49152
 CHAIN_MAX_K = 24576
 IN_X, IN_RMS, IN_GELU_RMS, IN_SILU_MUL = 0, 1, 2, 3
+OUT_Y, OUT_GELU = 0, 1
 
 QG_OK = 0
 STATUS = {
@@ -80,6 +81,8 @@ def lib():
         "qgemv_weight_bytes": ([_i32, _i64, _i64], _i64),
         "qgemv_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
+        "qgemv_rows_op": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _i64, _vp],
+                          ctypes.c_int),
         "qgemv_expert_windows": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _i64, _vp, _i64, _vp],
                                  ctypes.c_int),
         "qgemv_silu_mul": ([_vp, _vp, _vp, _i64, _vp], ctypes.c_int),
@@ -199,6 +202,18 @@ def qgemv_rows(w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 
     n = max(row_end - row_start, 0)
     _check(lib().qgemv_rows(ctypes.byref(m), row_start, row_end, _f32(x, w.k, "x"), _f32(y, n, "y"),
                             block_rows, _stream(stream)), "qgemv_rows")
+
+
+def qgemv_rows_op(w: Matrix, row_start: int, row_end: int, x, y, in_op: int = 0, eps: float = 0.0,
+                  out_op: int = 0, x2=None, block_rows: int = 0, stream=None) -> None:
+    """As qgemv_rows with a fused input transform (IN_X, IN_RMS, IN_SILU_MUL with ``x2``)
+    and output transform (OUT_Y, OUT_GELU)."""
+    m = w.c()
+    n = max(row_end - row_start, 0)
+    x2p = _f32(x2, w.k, "x2") if x2 is not None else None
+    _check(lib().qgemv_rows_op(ctypes.byref(m), row_start, row_end, _f32(x, w.k, "x"), x2p, int(in_op),
+                               float(eps), int(out_op), _f32(y, n, "y"), block_rows, _stream(stream)),
+           "qgemv_rows_op")
 
 
 def qgemv_windows(windows: Sequence[Window], block_rows: int = 0, stream=None, fmt=None, k=None) -> None:

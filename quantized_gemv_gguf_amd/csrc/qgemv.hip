@@ -145,6 +145,7 @@ template <> struct Fmt<QG_MXFP4> {
 struct WinDev {
   const uint8_t *base;  // row 0 of the window's matrix (16-byte aligned)
   const float *x;
+  const float *x2;      // the multiplier of QG_IN_SILU_MUL, else unused
   float *y;             // y[r - row_start] <-> row r
   int64_t row_start, row_end;
 };
@@ -155,6 +156,9 @@ struct GemvArgs {
   int64_t row_bytes;
   int64_t block_rows;  // > 0 (the host replaces 0 by a bound above every window)
   int32_t n_win, nb, tile_rows, n_tiles;
+  int32_t in_op;   // QG_IN_X, QG_IN_RMS or QG_IN_SILU_MUL: applied as x is loaded
+  int32_t out_op;  // QG_OUT_Y or QG_OUT_GELU: applied as y is stored
+  float eps;       // of QG_IN_RMS
 };
 
 // Sum over the 64 lanes of a wave in a fixed order (DPP row shifts, then row
@@ -174,6 +178,14 @@ __device__ __forceinline__ float wave_sum63(float v) {
   v += dpp_f<0x143, 0xc, 0xf>(v);  // row_bcast:31
   return v;
 }
+
+// Exact (erf) GELU, evaluated as 0.5 t erfc(-t / sqrt 2): equal to
+// 0.5 t (1 + erf(t / sqrt 2)), without that form's cancellation for t far
+// below 0 (which an RMS normalisation of small GELU values would magnify).
+__device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * erfcf(-t * 0.70710678118654752f); }
+
+// silu(g) * u, as qgemv_silu_mul computes it.
+__device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // One wave's partial sum for one staged row: lane l dots blocks l + 64c
 // (c < C) of the wave's slice, staged at byte `ph` of `sb`, with its
@@ -270,6 +282,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   constexpr int SB = 64 * C;  // blocks per slice
   __shared__ __attribute__((aligned(16))) uint8_t ring[WT][NS][SLOT];
   __shared__ float red[2][WT][kGemvTileRows];
+  __shared__ float ssq[WT * C];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -291,7 +304,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     int w, t0, t1;  // window index, its tiles [t0, t1)
     int64_t row_start, row_end;
     const uint8_t *base;  // row 0, advanced to the wave's slice
-    const float *x;
+    const float *x, *x2;
     float *y;
   };
   auto load_win = [&](int w, Win &W) {
@@ -302,6 +315,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     W.row_end = a.win[w].row_end;
     W.base = a.win[w].base + slice_off;
     W.x = a.win[w].x;
+    W.x2 = a.win[w].x2;
     W.y = a.win[w].y;
   };
   struct Tile {
@@ -342,8 +356,17 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     for (int v = 0; v < V; ++v) dma16(pa, min(lane16 + 1024u * v, last16), l + 1024u * v);
   };
 
+  // The team's activations: lane l of wave w holds the 32 inputs of block
+  // column w*64*C + l + 64*c in xr[c], zero past the row.  The input
+  // transforms are those of the separate calls, in the same order, so a
+  // fused launch gives their bits: silu(x) * x2 elementwise as qgemv_silu_mul;
+  // rms(x) with the sum of squares formed as qgemv_rms_carry forms it (32
+  // consecutive inputs per lane in order, the lanes of a 64-column run by
+  // wave_sum63, the runs in column order -- the team's waves cover every
+  // column, so no extra read), then one scale per input.
   float xr[C][32];
-  auto load_x = [&](const float *x) {
+  const int in_op = a.in_op;
+  auto load_x = [&](const float *x, const float *x2) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int j = slice_b0 + lane + 64 * c;
@@ -352,12 +375,40 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       for (int q = 0; q < 8; ++q) {
         float4 v;
         __builtin_memcpy(&v, x + 32 * jj + 4 * q, 16);
+        if (in_op == QG_IN_SILU_MUL) {
+          float4 u;
+          __builtin_memcpy(&u, x2 + 32 * jj + 4 * q, 16);
+          v.x = silu_times(v.x, u.x);
+          v.y = silu_times(v.y, u.y);
+          v.z = silu_times(v.z, u.z);
+          v.w = silu_times(v.w, u.w);
+        }
         const bool ok = j < nb;
         xr[c][4 * q + 0] = ok ? v.x : 0.0f;
         xr[c][4 * q + 1] = ok ? v.y : 0.0f;
         xr[c][4 * q + 2] = ok ? v.z : 0.0f;
         xr[c][4 * q + 3] = ok ? v.w : 0.0f;
       }
+    }
+    if (in_op == QG_IN_RMS) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ss = fmaf(xr[c][e], xr[c][e], ss);
+        ss = wave_sum63(ss);
+        if (lane == 63) ssq[C * wave + c] = ss;
+      }
+      __syncthreads();
+      float tot = 0.0f;
+#pragma unroll
+      for (int v = 0; v < C * WT; ++v) tot += ssq[v];
+      const float inv = 1.0f / sqrtf(tot / (float)(32 * nb) + a.eps);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) xr[c][e] *= inv;
+      __syncthreads();  // ssq is read before a later window rewrites it
     }
   };
 
@@ -378,7 +429,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     if (F.t + T < a.n_tiles) { locate(F.t + T, FW, F); fi = 0; }
     else f_end = true;
   };
-  load_x(CW.x);  // before the ring's first copies: its wait then drains nothing else
+  load_x(CW.x, CW.x2);  // before the ring's first copies: its wait then drains nothing else
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
     issue(FW, F, fi, s);
@@ -389,7 +440,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   int parity = 0;
   for (;;) {
     if (CW.w != xw) {
-      load_x(CW.x);
+      load_x(CW.x, CW.x2);
       xw = CW.w;
     }
     const int nrows = cur.nrows;
@@ -412,11 +463,12 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       }
     }
     float *yt = CW.y + (cur.r0 - CW.row_start);
+    const bool gelu_out = a.out_op == QG_OUT_GELU;
     if (WT == 1) {
       if (lane == 63) {
 #pragma unroll
         for (int i = 0; i < kGemvTileRows; ++i)
-          if (i < nrows) yt[i] = acc[i];
+          if (i < nrows) yt[i] = gelu_out ? gelu_erf(acc[i]) : acc[i];
       }
     } else {
       if (lane == 63) {
@@ -428,7 +480,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
         float s = red[parity][0][threadIdx.x];
 #pragma unroll
         for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
-        yt[threadIdx.x] = s;
+        yt[threadIdx.x] = gelu_out ? gelu_erf(s) : s;
       }
       parity ^= 1;
     }
@@ -473,11 +525,8 @@ __global__ void silu_mul_kernel(const float *g, const float *u, float *h, int64_
 }
 
 constexpr int kCarryThreads = 1024;
+constexpr int kMaxRmsK = 32 * kCarryThreads;  // largest k whose fused RMS matches qgemv_rms_carry's order
 
-// Exact (erf) GELU, evaluated as 0.5 t erfc(-t / sqrt 2): equal to
-// 0.5 t (1 + erf(t / sqrt 2)), without that form's cancellation for t far
-// below 0 (which an RMS normalisation of small GELU values would magnify).
-__device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * erfcf(-t * 0.70710678118654752f); }
 
 // One workgroup, 16 waves.  For n a multiple of 32 up to 32768 (every k a
 // GEMV takes in one pass), thread t owns elements [32t, 32t + 32): it loads
@@ -665,7 +714,6 @@ __device__ __forceinline__ void chain_wait(ChainSync *sy, unsigned target, bool 
   __syncthreads();
 }
 
-__device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // Pointers read from the chain's device tables lose their address space; the
 // kernel marks them global so that loads and stores are global_* (flat ones
@@ -1223,16 +1271,22 @@ GemvFn pick(int32_t fmt, Shape s) {
 // CUs * gemv_teams_per_cu(fmt, WT) teams, team b taking tiles b, b + T, ...; tiles
 // hold up to kGemvTileRows rows, fewer when the rows are too few to give every
 // team a tile, and never cross a row block.
+// in_op / out_op / eps: the fused transforms (QG_IN_X, QG_OUT_Y: none); x2[i]
+// is window i's SiLU multiplier (x2 may be null when in_op is not
+// QG_IN_SILU_MUL).
 int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
-                hipStream_t stream) {
+                hipStream_t stream, int32_t in_op = QG_IN_X, float eps = 0.0f, int32_t out_op = QG_OUT_Y,
+                const float *const *x2 = nullptr) {
   Shape s;
   int rc = team_shape(fmt, k, &s);
   if (rc) return rc;
   qg_window win[kMaxWindows];
+  const float *wx2[kMaxWindows];
   int n = 0;
   int64_t maxlen = 1, total = 0;
   for (int i = 0; i < n_in; ++i) {
     if (win_in[i].row_end == win_in[i].row_start) continue;
+    wx2[n] = x2 ? x2[i] : nullptr;
     win[n++] = win_in[i];
     maxlen = std::max<int64_t>(maxlen, win_in[i].row_end - win_in[i].row_start);
     total += win_in[i].row_end - win_in[i].row_start;
@@ -1251,6 +1305,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
     const int64_t full = len / B, rem = len - full * B;
     a.win[i].base = (const uint8_t *)win[i].data;
     a.win[i].x = win[i].x;
+    a.win[i].x2 = wx2[i];
     a.win[i].y = win[i].y;
     a.win[i].row_start = win[i].row_start;
     a.win[i].row_end = win[i].row_end;
@@ -1265,6 +1320,9 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   a.block_rows = B;
   a.tile_rows = tile_rows;
   a.n_tiles = (int32_t)tiles;
+  a.in_op = in_op;
+  a.out_op = out_op;
+  a.eps = eps;
   const int64_t teams = std::min<int64_t>(teams_max, tiles);
   hipLaunchKernelGGL(pick(fmt, s), dim3((unsigned)teams), dim3(64 * s.wt), 0, stream, a);
   QG_HIP(hipGetLastError());
@@ -1347,6 +1405,21 @@ int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const flo
   if (!x || !y) return QG_E_NULL;
   qg_window win = {w->data, w->n_rows, row_start, row_end, x, y};
   return launch_gemv(w->fmt, w->k, &win, 1, block_rows, stream);
+}
+
+int qgemv_rows_op(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, const float *x2,
+                  int32_t in_op, float eps, int32_t out_op, float *y, int64_t block_rows, qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  if (block_rows < 0) return QG_E_ARG;
+  if (in_op != QG_IN_X && in_op != QG_IN_RMS && in_op != QG_IN_SILU_MUL) return QG_E_ARG;
+  if (out_op != QG_OUT_Y && out_op != QG_OUT_GELU) return QG_E_ARG;
+  if (in_op == QG_IN_RMS && (!(eps >= 0.0f) || eps > 3.0e38f || w->k > kMaxRmsK)) return QG_E_ARG;
+  if (row_end == row_start) return QG_OK;
+  if (!x || !y || (in_op == QG_IN_SILU_MUL && !x2)) return QG_E_NULL;
+  qg_window win = {w->data, w->n_rows, row_start, row_end, x, y};
+  return launch_gemv(w->fmt, w->k, &win, 1, block_rows, stream, in_op, eps, out_op, &x2);
 }
 
 int qgemv_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win, int64_t block_rows,

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -46,6 +46,7 @@ def test_header_constants_match_binding():
     assert f"#define QG_CHAIN_MAX_K {q.CHAIN_MAX_K}" in text
     assert re.search(rf"QG_IN_X = {q.IN_X}, QG_IN_RMS = {q.IN_RMS}, QG_IN_GELU_RMS = {q.IN_GELU_RMS}, "
                      rf"QG_IN_SILU_MUL = {q.IN_SILU_MUL}", text)
+    assert re.search(rf"QG_OUT_Y = {q.OUT_Y}, QG_OUT_GELU = {q.OUT_GELU}", text)
     for code, name in q.STATUS.items():
         assert re.search(rf"{name} = {code}\b", text), name
 
@@ -181,6 +182,30 @@ def test_streamer_validation():
     assert L.qgemv_stream_destroy(None) == 0
     assert L.qgemv_stream_rows(None, ctypes.byref(mat()), 0, 8, 0, FAKE, FAKE, None) == E_NULL
     assert L.qgemv_stream_windows(None, 1, 64, None, 0, 0, None) == E_NULL
+
+
+def test_rows_op_validation():
+    L = q.lib()
+
+    def call(m=None, r0=0, r1=8, x=FAKE, x2=FAKE, in_op=0, eps=1e-6, out_op=0, y=FAKE, B=0, k=64):
+        m = mat(k=k) if m is None else m
+        return L.qgemv_rows_op(ctypes.byref(m), r0, r1, x, x2, in_op, eps, out_op, y, B, None)
+
+    assert L.qgemv_rows_op(None, 0, 8, FAKE, FAKE, 0, 0.0, 0, FAKE, 0, None) == E_NULL
+    assert call(m=mat(fmt=5)) == E_FMT
+    assert call(r1=9) == E_RANGE
+    assert call(B=-1) == E_ARG
+    assert call(in_op=2) == E_ARG  # GELU_RMS: GELU belongs to the producer (QG_OUT_GELU)
+    assert call(in_op=4) == E_ARG and call(in_op=-1) == E_ARG
+    assert call(out_op=2) == E_ARG
+    assert call(in_op=1, eps=-1.0) == E_ARG
+    assert call(in_op=1, eps=float("nan")) == E_ARG
+    assert call(in_op=1, eps=float("inf")) == E_ARG
+    big = 32768 + 32
+    assert call(m=mat(k=big), in_op=1, k=big) == E_ARG  # fused RMS only where it matches qgemv_rms_carry
+    assert call(x=0) == E_NULL and call(y=0) == E_NULL
+    assert call(in_op=3, x2=0) == E_NULL
+    assert call(r0=4, r1=4, x=0, y=0) == 0
 
 
 def test_mapped_validation():
