@@ -188,12 +188,15 @@ class DensePass:
     def reset_fused(self):
         self.d.copy_(self.x0)
 
-    def token_fused(self, events=None, hook=None, stream=None):
+    def token_fused(self, events=None, hook=None, stream=None, only=None):
         """One token as 176 fused GEMV launches (qgemv_rows_op).  events: one
-        (start, end) pair per GEMV, recorded around it on the launch stream."""
+        (start, end) pair per GEMV, recorded around it on the launch stream;
+        only: indices of the launches to issue (timing of one kernel variant)."""
         L, q = self.lib, self.q
         st = self.stream if stream is None else stream
         for i, (mp, r, xp, yp, nbytes, k, m, out_op) in enumerate(self.fcalls):
+            if only is not None and i not in only:
+                continue
             if events is not None:
                 events[i][0].record()
             rc = L.qgemv_rows_op(mp, 0, r, xp, None, q.IN_RMS, self.eps, out_op, yp, 0, st)
@@ -269,22 +272,20 @@ def dense_workload(args, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = g0.elapsed_time(g1)
-    # per-launch durations (HIP events around every launch on its stream), from
-    # eager tokens after the timed region, grouped by kernel variant (k decides it)
-    n_ev = max(2, min(args.steps, 8))
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-              for _ in range(n_ev)]
-    for s in range(n_ev):
-        model.token_fused(events[s])
-    torch.cuda.synchronize()
+    # per-kernel durations: right after the timed region, each kernel variant's
+    # launches of two tokens run back to back on the launch stream, bracketed by
+    # one pair of HIP events (an event pair around every single launch would
+    # add its own packets and gaps to each measured launch)
     per_k = {}
-    for s in range(n_ev):
-        for i, (mp, r, xp, yp, nbytes, k, m, _) in enumerate(model.fcalls):
-            ms = events[s][i][0].elapsed_time(events[s][i][1])
-            e = per_k.setdefault(k, [0, 0.0, 0])
-            e[0] += nbytes
-            e[1] += ms
-            e[2] += 1
+    for kk in sorted({c_[5] for c_ in model.fcalls}):
+        sub = [i for i, c_ in enumerate(model.fcalls) if c_[5] == kk]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            model.token_fused(only=sub)
+        e1.record()
+        torch.cuda.synchronize()
+        per_k[kk] = [2 * sum(model.fcalls[i][4] for i in sub), e0.elapsed_time(e1), 2 * len(sub)]
     total_bytes = model.bytes_per_token * args.steps
     gbs = total_bytes / wall / 1e9
     kernels = {}
