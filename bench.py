@@ -41,16 +41,26 @@ HBM_PEAK_GBS = 8000.0
 TOL = 1e-4
 
 
+def kernel_source_sha256():
+    """SHA-256 over every kernel source file, in build order."""
+    import hashlib
+    from quantized_gemv_gguf_amd import build as qb
+    h = hashlib.sha256()
+    try:
+        for path in qb.source_paths():
+            h.update(open(path, "rb").read())
+    except OSError:
+        return None
+    return h.hexdigest()
+
+
 def profiled_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from a committed rocprofv3 counter
     summary (profiles/*_hbm_traffic.md), if it was taken on the kernel source
     as it is now; else None."""
     import glob
-    import hashlib
-    src = os.path.join(ROOT, "quantized_gemv_gguf_amd", "csrc", "qgemv.hip")
-    try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except OSError:
+    sha = kernel_source_sha256()
+    if sha is None:
         return None
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
         vals = {}

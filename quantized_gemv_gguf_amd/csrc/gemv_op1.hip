@@ -1,0 +1,7 @@
+// gemv_op1.hip -- instantiates the GEMV kernels of fused-transform variant
+// kOpRms (every format and team shape); see qgemv_impl.h.
+#include "qgemv_impl.h"
+
+namespace qgemv_detail {
+template GemvFn pick_op<kOpRms>(int32_t, Shape);
+}  // namespace qgemv_detail

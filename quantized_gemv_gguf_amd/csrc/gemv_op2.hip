@@ -1,0 +1,7 @@
+// gemv_op2.hip -- instantiates the GEMV kernels of fused-transform variant
+// kOpRmsGelu (every format and team shape); see qgemv_impl.h.
+#include "qgemv_impl.h"
+
+namespace qgemv_detail {
+template GemvFn pick_op<kOpRmsGelu>(int32_t, Shape);
+}  // namespace qgemv_detail

@@ -1,0 +1,516 @@
+// qgemv_impl.h -- gfx950 GEMV kernel templates shared by libqgemv.so's
+// translation units: the block formats, the fused row dot, the GEMV kernel and
+// its launch-shape picker.  Each fused-transform variant of the GEMV kernel is
+// instantiated in a translation unit of its own (gemv_op*.hip), so the library
+// builds in parallel; qgemv.hip holds the chain kernel and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <stdint.h>
+
+#include <utility>
+
+#include "qgemv.h"
+
+namespace qgemv_detail {
+
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxWindows = QG_MAX_WINDOWS;
+constexpr int kMaxC = 2;         // block columns per lane
+constexpr int kMaxWT = 12;       // waves per team
+
+// ---------------------------------------------------------------------------
+// Formats.  A block is a scale field followed by a payload of kWords 32-bit
+// words.  decode() turns the payload into 32 "unit" values u_j and scale()
+// the scale field into a Scale such that the weight is w_j = apply(scale, u_j);
+// the GEMV applies the scale once to a block's partial dot product, the
+// dequant kernel applies it to every u_j.  Both use the same decoder, so the
+// bit-exact decode check covers the GEMV's decoder.
+// ---------------------------------------------------------------------------
+
+template <int FMT> struct Fmt;
+
+// Q8_0: fp16 d, 32 x int8 q; w = d * q (RAMforge README, "Milestone 5").
+template <> struct Fmt<QG_Q8_0> {
+  static constexpr int kBytes = 34, kScaleBytes = 2, kWords = 8;
+  struct Scale { float d; };
+  __device__ static inline Scale scale(uint32_t bits) {
+    return Scale{__half2float(__ushort_as_half((uint16_t)bits))};
+  }
+  __device__ static inline void decode(const uint32_t *q, float u[32]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[4 * i + k] = (float)(int8_t)(q[i] >> (8 * k));
+    }
+  }
+  __device__ static inline float apply(Scale s, float v) { return s.d * v; }
+  __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d, v, acc); }
+};
+
+// Q4_0: fp16 d, 16 bytes of nibbles; w = d * (q - 8) (RAMforge README,
+// "Milestone 5").  Element j < 16 is the low nibble of byte j, element j + 16
+// the high nibble.  (q ^ 8) is q - 8 in 4-bit two's complement; moved to the
+// top of a byte it reads as the int8 16 * (q - 8), exactly, and the 1/16 goes
+// into the scale (a power of two, so d/16 is exact too).
+template <> struct Fmt<QG_Q4_0> {
+  static constexpr int kBytes = 18, kScaleBytes = 2, kWords = 4;
+  struct Scale { float d16; };
+  __device__ static inline Scale scale(uint32_t bits) {
+    return Scale{__half2float(__ushort_as_half((uint16_t)bits)) * 0.0625f};
+  }
+  __device__ static inline void decode(const uint32_t *q, float u[32]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = q[i] ^ 0x88888888u;
+      const uint32_t hi = v & 0xF0F0F0F0u;
+      const uint32_t lo = (v << 4) & 0xF0F0F0F0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u[4 * i + k] = (float)(int8_t)(lo >> (8 * k));
+        u[16 + 4 * i + k] = (float)(int8_t)(hi >> (8 * k));
+      }
+    }
+  }
+  __device__ static inline float apply(Scale s, float v) { return s.d16 * v; }
+  __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d16, v, acc); }
+};
+
+// MXFP4: E8M0 e, 16 bytes of E2M1 nibbles; w = 2^(e-127) * E2M1(nib) (block
+// size from neurostream README, "The idea": 4.41 MB per 2,880 x 2,880 expert).
+// gfx950's v_cvt_scalef32_pk_f32_fp4 turns both nibbles of a byte into fp32
+// (scale 1.0: the E2M1 value itself, exact); the E8M0 scale is applied with an
+// exact ldexp, and e = 255 gives NaN.
+template <> struct Fmt<QG_MXFP4> {
+  static constexpr int kBytes = 17, kScaleBytes = 1, kWords = 4;
+  struct Scale { int e; };
+  __device__ static inline Scale scale(uint32_t bits) { return Scale{(int)(bits & 0xffu)}; }
+  // f = (value of the byte's low nibble, value of its high nibble)
+  template <typename V2>
+  __device__ static inline void unpack(V2 f, float *u) {
+    u[0] = f[0];
+    u[16] = f[1];
+  }
+  __device__ static inline void decode(const uint32_t *q, float u[32]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 0), u + 4 * i + 0);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 1), u + 4 * i + 1);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 2), u + 4 * i + 2);
+      unpack(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 3), u + 4 * i + 3);
+    }
+  }
+  __device__ static inline float apply(Scale s, float v) {
+    return s.e == 255 ? __builtin_nanf("") : ldexpf(v, s.e - 127);
+  }
+  __device__ static inline float fma_acc(Scale s, float v, float acc) { return acc + apply(s, v); }
+};
+
+// ---------------------------------------------------------------------------
+// GEMV kernel
+// ---------------------------------------------------------------------------
+
+struct WinDev {
+  const uint8_t *base;  // row 0 of the window's matrix (16-byte aligned)
+  const float *x;
+  const float *x2;      // the multiplier of QG_IN_SILU_MUL, else unused
+  float *y;             // y[r - row_start] <-> row r
+  int64_t row_start, row_end;
+};
+
+struct GemvArgs {
+  WinDev win[kMaxWindows];
+  int32_t tile_prefix[kMaxWindows + 1];  // tiles of windows [0, w)
+  int64_t row_bytes;
+  int64_t block_rows;  // > 0 (the host replaces 0 by a bound above every window)
+  int32_t n_win, nb, tile_rows, n_tiles;
+  int32_t in_op;   // QG_IN_X, QG_IN_RMS or QG_IN_SILU_MUL: applied as x is loaded
+  int32_t out_op;  // QG_OUT_Y or QG_OUT_GELU: applied as y is stored
+  float eps;       // of QG_IN_RMS
+};
+
+// Sum over the 64 lanes of a wave in a fixed order (DPP row shifts, then row
+// broadcasts); the total lands in lane 63.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK,
+                                                               BANK_MASK, false));
+}
+
+__device__ __forceinline__ float wave_sum63(float v) {
+  v += dpp_f<0x111, 0xf, 0xf>(v);  // row_shr:1
+  v += dpp_f<0x112, 0xf, 0xf>(v);  // row_shr:2
+  v += dpp_f<0x114, 0xf, 0xe>(v);  // row_shr:4
+  v += dpp_f<0x118, 0xf, 0xc>(v);  // row_shr:8
+  v += dpp_f<0x142, 0xa, 0xf>(v);  // row_bcast:15
+  v += dpp_f<0x143, 0xc, 0xf>(v);  // row_bcast:31
+  return v;
+}
+
+// Exact (erf) GELU, evaluated as 0.5 t erfc(-t / sqrt 2): equal to
+// 0.5 t (1 + erf(t / sqrt 2)), without that form's cancellation for t far
+// below 0 (which an RMS normalisation of small GELU values would magnify).
+__device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * erfcf(-t * 0.70710678118654752f); }
+
+// silu(g) * u, as qgemv_silu_mul computes it.
+__device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// One wave's partial sum for one staged row: lane l dots blocks l + 64c
+// (c < C) of the wave's slice, staged at byte `ph` of `sb`, with its
+// registered activations.  Fixed order: four FMA chains per block combined
+// as (p0 + p1) + (p2 + p3), the block scale applied once, blocks in c order.
+template <int FMT, int C>
+__device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane, int slice_n,
+                                             const float (&xr)[C][32]) {
+  using F = Fmt<FMT>;
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int b = lane + 64 * c;
+    const int bo = ph + F::kBytes * b;  // block's byte offset in the staged row
+    // LDS reads at any byte alignment (gfx950 serves unaligned DS accesses):
+    // the payload needs no realignment in registers.
+    uint32_t sbits = 0, q[F::kWords];
+    __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
+    __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
+    float u[32];
+    F::decode(q, u);
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
+    const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
+    s = b < slice_n ? blk_acc : s;
+  }
+  return s;
+}
+
+// Largest rows per chain tile, per (format, block columns per lane): a chain
+// wave holds its tile's fetched rows in registers until staged.
+template <int FMT, int C> struct TileCap { static constexpr int value = 1; };
+template <> struct TileCap<QG_Q8_0, 1> { static constexpr int value = 6; };
+template <> struct TileCap<QG_Q8_0, 2> { static constexpr int value = 2; };
+template <> struct TileCap<QG_Q4_0, 1> { static constexpr int value = 8; };
+template <> struct TileCap<QG_Q4_0, 2> { static constexpr int value = 4; };
+template <> struct TileCap<QG_MXFP4, 1> { static constexpr int value = 8; };
+template <> struct TileCap<QG_MXFP4, 2> { static constexpr int value = 4; };
+
+// Weight staging of gemv_kernel: a wave's slice of a row is copied from HBM
+// straight into its LDS ring (gfx950 global_load_lds_dwordx4: lane l's 16
+// bytes land at M0 + 16 l), V loads per row, each a whole aligned 16-byte
+// granule per lane.  Lanes past the slice's last granule re-read that granule
+// into their own place beyond the data, so every load is unconditional and
+// the number of loads per row is a constant the waits can count.
+template <int FMT, int C> struct Geo {
+  static constexpr int CH = (15 + 64 * C * Fmt<FMT>::kBytes + 15) / 16;  // granules a slice can touch
+  static constexpr int V = (CH + 63) / 64;                               // loads per lane per row
+  static constexpr int SLOT = 1024 * V;                                  // ring slot bytes
+};
+
+// Concurrency of gemv_kernel, a function of (format, team size): Q8_0 runs
+// about six waves per compute unit, each with two rows in flight while it
+// computes one more; the 4-bit formats, with twice the decode work per byte,
+// run twelve waves with one row in flight.  More requests in flight than that
+// (more waves, deeper rings) made the same walks slower on MI355X: HBM serves
+// a compact, moderate stream better than a wide, deep one.
+__host__ __device__ constexpr int gemv_waves_per_cu(int fmt) { return fmt == QG_Q8_0 ? 6 : 12; }
+__host__ __device__ constexpr int gemv_teams_per_cu(int fmt, int wt) {
+  return wt >= gemv_waves_per_cu(fmt) ? 1 : gemv_waves_per_cu(fmt) / wt;
+}
+__host__ __device__ constexpr int gemv_in_flight(int fmt, int wt) {
+  return fmt == QG_Q8_0 && wt * gemv_teams_per_cu(fmt, wt) <= 6 ? 2 : 1;
+}
+constexpr int kGemvTileRows = 8;  // most rows per tile
+
+// One asynchronous 16-byte HBM -> LDS copy per lane: global_load_lds_dwordx4
+// with a scalar base, a 32-bit lane offset and the LDS destination in M0.
+// Written as inline assembly because the compiler's own waits for LDS DMA
+// drain every outstanding load before any LDS read; here the kernel counts
+// its loads and waits with s_waitcnt vmcnt itself.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// One team = WT waves.  Wave w owns the contiguous block columns
+// [w*64*C, (w+1)*64*C) of every row (its "slice"), lane l the columns
+// w*64*C + l + 64*c, whose 32 activations each it keeps in registers.
+// A tile is up to tile_rows rows of one row block; team b takes tiles
+// b, b + T, b + 2T, ... (T teams), so at any moment the grid works on a
+// compact band of the matrix.  Each wave streams its slices row after row
+// through an LDS ring of NB + 1 slots: before computing a row it issues the
+// copy of the row NB ahead (crossing tiles), so NB rows are in flight while
+// it decodes.  The team's per-wave row sums meet in LDS and are added in
+// wave order.
+// The fused transforms a launch applies, fixed at compile time: code for an
+// op a launch does not use (even behind a runtime branch) made the plain GEMV
+// up to 17% slower.
+enum GemvOp { kOpNone = 0, kOpRms = 1, kOpRmsGelu = 2, kOpSilu = 3, kOpGelu = 4 };
+__host__ __device__ constexpr int op_in(int op) {
+  return op == kOpRms || op == kOpRmsGelu ? QG_IN_RMS : op == kOpSilu ? QG_IN_SILU_MUL : QG_IN_X;
+}
+__host__ __device__ constexpr bool op_gelu(int op) { return op == kOpRmsGelu || op == kOpGelu; }
+
+template <int FMT, int WT, int C, int OP>
+__global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
+  using G = Geo<FMT, C>;
+  constexpr int V = G::V, SLOT = G::SLOT;
+  constexpr int NB = gemv_in_flight(FMT, WT), NS = NB + 1;
+  constexpr int SB = 64 * C;  // blocks per slice
+  __shared__ __attribute__((aligned(16))) uint8_t ring[WT][NS][SLOT];
+  __shared__ float red[2][WT][kGemvTileRows];
+  __shared__ float ssq[WT * C];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int nb = a.nb;
+  const int64_t rb = a.row_bytes;
+  const int slice_b0 = wave * SB;
+  const int slice_n = max(0, min(SB, nb - slice_b0));  // >= 1 by the choice of WT
+  const int64_t slice_off = (int64_t)slice_b0 * Fmt<FMT>::kBytes;
+  const uint32_t slice_len = (uint32_t)slice_n * Fmt<FMT>::kBytes;
+  const int T = gridDim.x;
+  if ((int)blockIdx.x >= a.n_tiles) return;
+
+  // Kernel-argument fields used in the loop are read once into registers, and
+  // a window's fields again only when a cursor enters the next window.
+  const int64_t B = a.block_rows;
+  const int TR = a.tile_rows;
+  const int tpb = (int)((B + TR - 1) / TR);
+  struct Win {
+    int w, t0, t1;  // window index, its tiles [t0, t1)
+    int64_t row_start, row_end;
+    const uint8_t *base;  // row 0, advanced to the wave's slice
+    const float *x, *x2;
+    float *y;
+  };
+  auto load_win = [&](int w, Win &W) {
+    W.w = w;
+    W.t0 = a.tile_prefix[w];
+    W.t1 = a.tile_prefix[w + 1];
+    W.row_start = a.win[w].row_start;
+    W.row_end = a.win[w].row_end;
+    W.base = a.win[w].base + slice_off;
+    W.x = a.win[w].x;
+    W.x2 = a.win[w].x2;
+    W.y = a.win[w].y;
+  };
+  struct Tile {
+    int t, nrows;
+    int64_t r0;
+  };
+  // Tile t of window W (advanced to the window holding t).
+  auto locate = [&](int t, Win &W, Tile &Q) {
+    if (t >= W.t1) {
+      int w = W.w + 1;
+      while (t >= a.tile_prefix[w + 1]) ++w;
+      load_win(w, W);
+    }
+    const int tt = t - W.t0;
+    // Row block and tile within it; a window of one row block (block_rows 0)
+    // needs no division.
+    int blk = 0, tib = tt;
+    if (tt >= tpb) {
+      blk = tt / tpb;
+      tib = tt - blk * tpb;
+    }
+    Q.t = t;
+    Q.r0 = W.row_start + (int64_t)blk * B + (int64_t)tib * TR;
+    const int64_t r1 = min(Q.r0 + TR, min(W.row_start + (int64_t)(blk + 1) * B, W.row_end));
+    Q.nrows = (int)(r1 - Q.r0);
+  };
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
+  const uint32_t lane16 = 16u * lane;
+  // Copy the wave's slice of the row at p (any byte alignment) into ring slot s.
+  auto issue = [&](const uint8_t *p, int s) {
+    const uint32_t ph = (uint32_t)((uintptr_t)p & 15);
+    const uint32_t last16 = ((ph + slice_len - 1) >> 4) << 4;
+    const uint8_t *pa = p - ph;
+    const uint32_t l = lds0 + SLOT * s;
+#pragma unroll
+    for (int v = 0; v < V; ++v) dma16(pa, min(lane16 + 1024u * v, last16), l + 1024u * v);
+  };
+
+  // The team's activations: lane l of wave w holds the 32 inputs of block
+  // column w*64*C + l + 64*c in xr[c], zero past the row.  The input
+  // transforms are those of the separate calls, in the same order, so a
+  // fused launch gives their bits: silu(x) * x2 elementwise as qgemv_silu_mul;
+  // rms(x) with the sum of squares formed as qgemv_rms_carry forms it (32
+  // consecutive inputs per lane in order, the lanes of a 64-column run by
+  // wave_sum63, the runs in column order -- the team's waves cover every
+  // column, so no extra read), then one scale per input.
+  float xr[C][32];
+  constexpr int in_op = op_in(OP);
+  auto load_x = [&](const float *x, const float *x2) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = slice_b0 + lane + 64 * c;
+      const int jj = min(j, nb - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float4 v;
+        __builtin_memcpy(&v, x + 32 * jj + 4 * q, 16);
+        if constexpr (in_op == QG_IN_SILU_MUL) {
+          float4 u;
+          __builtin_memcpy(&u, x2 + 32 * jj + 4 * q, 16);
+          v.x = silu_times(v.x, u.x);
+          v.y = silu_times(v.y, u.y);
+          v.z = silu_times(v.z, u.z);
+          v.w = silu_times(v.w, u.w);
+        }
+        const bool ok = j < nb;
+        xr[c][4 * q + 0] = ok ? v.x : 0.0f;
+        xr[c][4 * q + 1] = ok ? v.y : 0.0f;
+        xr[c][4 * q + 2] = ok ? v.z : 0.0f;
+        xr[c][4 * q + 3] = ok ? v.w : 0.0f;
+      }
+    }
+    if constexpr (in_op == QG_IN_RMS) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ss = fmaf(xr[c][e], xr[c][e], ss);
+        ss = wave_sum63(ss);
+        if (lane == 63) ssq[C * wave + c] = ss;
+      }
+      __syncthreads();
+      float tot = 0.0f;
+#pragma unroll
+      for (int v = 0; v < C * WT; ++v) tot += ssq[v];
+      const float inv = 1.0f / sqrtf(tot / (float)(32 * nb) + a.eps);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) xr[c][e] *= inv;
+      __syncthreads();  // ssq is read before a later window rewrites it
+    }
+  };
+
+  // Copy cursor: fp is the wave's slice of the next row to copy, f_left the
+  // rows left in its tile (F, window FW); both advance by one row per copy.
+  // Past the team's last row the cursor stays on that row, re-copying it into
+  // a slot no computation reads, which keeps one fixed count of loads per row.
+  Win CW, FW;
+  load_win(0, CW);
+  Tile cur, F;
+  locate(blockIdx.x, CW, cur);
+  FW = CW;
+  F = cur;
+  const uint8_t *fp = FW.base + F.r0 * rb;
+  int f_left = F.nrows;
+  bool f_end = false;
+  auto advance_fetch = [&]() {
+    if (f_end) return;
+    if (--f_left > 0) {
+      fp += rb;
+      return;
+    }
+    if (F.t + T < a.n_tiles) {
+      locate(F.t + T, FW, F);
+      fp = FW.base + F.r0 * rb;
+      f_left = F.nrows;
+    } else {
+      f_end = true;
+    }
+  };
+  load_x(CW.x, CW.x2);  // before the ring's first copies: its wait then drains nothing else
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    issue(fp, s);
+    advance_fetch();
+  }
+  int xw = CW.w;
+  int slot = 0;  // ring slot of the row being computed
+  int parity = 0;
+  for (;;) {
+    if (CW.w != xw) {
+      load_x(CW.x, CW.x2);
+      xw = CW.w;
+    }
+    const int nrows = cur.nrows;
+    // Alignment phase of the tile's rows: row i of the tile sits at
+    // (ph0 + i * rb) mod 16 within its first granule.
+    const uint32_t ph0 = (uint32_t)((uintptr_t)(CW.base + cur.r0 * rb) & 15);
+    const uint32_t rb16 = (uint32_t)(rb & 15);
+    float acc[kGemvTileRows];
+#pragma unroll
+    for (int i = 0; i < kGemvTileRows; ++i) {
+      acc[i] = 0.0f;
+      if (i < nrows) {
+        // The slot NB ahead held the previous row, whose LDS reads are done.
+        int s2 = slot + NB;
+        s2 = s2 >= NS ? s2 - NS : s2;
+        wait_lds_reads();
+        issue(fp, s2);
+        advance_fetch();
+        wait_vmcnt<V * NB>();  // this row's copies have landed
+        const uint8_t *sb = &ring[wave][slot][0];
+        const int ph = (int)((ph0 + (uint32_t)i * rb16) & 15);
+        acc[i] = wave_sum63(row_partial<FMT, C>(sb, ph, lane, slice_n, xr));
+        slot = slot + 1 == NS ? 0 : slot + 1;
+      }
+    }
+    float *yt = CW.y + (cur.r0 - CW.row_start);
+    constexpr bool gelu_out = op_gelu(OP);
+    if (WT == 1) {
+      if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < kGemvTileRows; ++i)
+          if (i < nrows) yt[i] = gelu_out ? gelu_erf(acc[i]) : acc[i];
+      }
+    } else {
+      if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < kGemvTileRows; ++i) red[parity][wave][i] = acc[i];
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < nrows) {
+        float s = red[parity][0][threadIdx.x];
+#pragma unroll
+        for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
+        yt[threadIdx.x] = gelu_out ? gelu_erf(s) : s;
+      }
+      parity ^= 1;
+    }
+    if (cur.t + T >= a.n_tiles) break;
+    locate(cur.t + T, CW, cur);
+  }
+  // The ring's last copies (re-reads past the end) must land before the
+  // workgroup's LDS is released.
+  wait_vmcnt<0>();
+}
+
+// Team shape (WT waves, C block columns per lane), a function of (format, k).
+struct Shape { int wt, c; };
+
+typedef void (*GemvFn)(GemvArgs);
+
+template <int FMT, int C, int OP, int... WT>
+GemvFn pick_wt(int wt, std::integer_sequence<int, WT...>) {
+  GemvFn fn = nullptr;
+  ((wt == WT + 1 ? (fn = gemv_kernel<FMT, WT + 1, C, OP>, 0) : 0), ...);
+  return fn;
+}
+
+template <int FMT, int OP>
+GemvFn pick_fmt(Shape s) {
+  if (s.c == 1) return pick_wt<FMT, 1, OP>(s.wt, std::make_integer_sequence<int, kMaxWT>{});
+  return pick_wt<FMT, 2, OP>(s.wt, std::make_integer_sequence<int, kMaxWT>{});
+}
+
+template <int OP>
+GemvFn pick_op(int32_t fmt, Shape s) {
+  switch (fmt) {
+    case QG_Q8_0: return pick_fmt<QG_Q8_0, OP>(s);
+    case QG_Q4_0: return pick_fmt<QG_Q4_0, OP>(s);
+    default: return pick_fmt<QG_MXFP4, OP>(s);
+  }
+}
+
+}  // namespace qgemv_detail
