@@ -1,4 +1,5 @@
-"""CPU oracle for the batch-1 dequant-GEMV over GGUF blocks (Q8_0, Q4_0, MXFP4).
+"""CPU oracle for the batch-1 dequant-GEMV over GGUF blocks (Q8_0, Q4_0, MXFP4,
+Q4_K, Q6_K).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
 CPU-baseline leg of the benchmark may import this module.  It shares no code
@@ -8,8 +9,10 @@ fp64 sums), built here with gcc and called through ctypes.
 Functions (each follows the passage cited in ``oracle.c``):
 
 * ``dequant_rows(fmt, w, n_rows, k, r0, r1)`` -> fp32 ``(r1-r0, k)``: the block
-  decoders of RAMforge README "Milestone 5" (Q8_0 ``d*q``, Q4_0 ``d*(q-8)``)
-  and the 17-byte MXFP4 block implied by neurostream README "The idea".
+  decoders of RAMforge README "Milestone 5" (Q8_0 ``d*q``, Q4_0 ``d*(q-8)``,
+  Q4_K ``d*sc*q - dmin*m`` over 256-weight super-blocks), the 17-byte MXFP4
+  block implied by neurostream README "The idea", and Q6_K in GGUF's layout
+  (the pages name it without printing its layout).
 * ``gemv_rows(fmt, w, n_rows, k, r0, r1, x)`` -> ``(y, a)`` in fp64, with
   ``y[j] = sum_i W[r0+j, i] x[i]`` (RAMforge README "Milestone 6", matrix
   layout) and ``a[j] = sum_i |W[r0+j, i] x[i]|``.
@@ -23,7 +26,7 @@ import subprocess
 
 import numpy as np
 
-Q8_0, Q4_0, MXFP4 = 1, 2, 3
+Q8_0, Q4_0, MXFP4, Q4_K, Q6_K = 1, 2, 3, 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -53,6 +56,8 @@ def load(path: str | None = None):
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     lib.orc_block_bytes.argtypes = [i32]
     lib.orc_block_bytes.restype = i64
+    lib.orc_block_weights.argtypes = [i32]
+    lib.orc_block_weights.restype = i64
     lib.orc_row_bytes.argtypes = [i32, i64]
     lib.orc_row_bytes.restype = i64
     lib.orc_half_to_double.argtypes = [ctypes.c_uint16]
@@ -78,6 +83,10 @@ def _ptr(a: np.ndarray) -> int:
 
 def block_bytes(fmt: int, lib=None) -> int:
     return int((lib or load()).orc_block_bytes(fmt))
+
+
+def block_weights(fmt: int, lib=None) -> int:
+    return int((lib or load()).orc_block_weights(fmt))
 
 
 def row_bytes(fmt: int, k: int, lib=None) -> int:

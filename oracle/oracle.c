@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain, slow, scalar CPU oracle for the batch-1 dequant-GEMV over
- * GGUF block-quantized weights (Q8_0, Q4_0, MXFP4).
+ * GGUF block-quantized weights (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
  * this file: only the test suite, the package's smoke check and the CPU-baseline
@@ -11,7 +11,8 @@
  *
  *   y[j] = sum_{i<K} dec(W)[row_start + j, i] * x[i],   j < row_end - row_start
  *
- * with W stored row-major as [n_rows][K/32 blocks] -- the GGML/GGUF matrix
+ * with W stored row-major as [n_rows][K/QK blocks] (QK = 32 weights per
+ * block; 256 for the K-quants) -- the GGML/GGUF matrix
  * convention that RAMforge's README states under "Milestone 6 - True
  * Out-of-Core Integrity" (shape [in, out], buffer [out][in], y[o] = sum_i
  * W[o*in + i] * x[i]).  Each row is a whole number of quantization blocks
@@ -27,6 +28,16 @@
  *   MXFP4: 17 bytes = E8M0 scale byte e, then 16 bytes of E2M1 nibbles;
  *          w = 2^(e-127) * E2M1(code)
  *
+ * K-quants, 256-weight super-blocks of eight 32-weight sub-blocks:
+ *   Q4_K : 144 bytes = fp16 d, fp16 dmin, 12 bytes holding eight 6-bit
+ *          sub-block scales sc and eight 6-bit mins m, 128 bytes of nibbles;
+ *          w = d * sc * q - dmin * m  (RAMforge README, "Milestone 5", Q4_K)
+ *   Q6_K : 210 bytes = 128 bytes of low nibbles, 64 bytes of 2-bit high
+ *          parts, sixteen int8 scales (one per 16 weights), fp16 d;
+ *          w = d * scale * (q - 32), q the 6-bit code (named by RAMforge README
+ *          "Milestone 5" and neurostream README "Supported"; the pages print
+ *          no layout for it)
+ *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of the repository):
  *   - nibble order: element j (j < 16) is the low nibble of qs[j], element
@@ -34,12 +45,25 @@
  *   - E2M1 is the OCP MX 4-bit float: 1 sign bit (bit 3), 2 exponent bits
  *     (bias 1), 1 mantissa bit; E8M0 is a bare biased exponent 2^(e-127) with
  *     e = 255 meaning NaN;
- *   - the fp16 scale is IEEE binary16, decoded here from its bit fields.
+ *   - the fp16 scale is IEEE binary16, decoded here from its bit fields;
+ *   - K-quant byte layouts are GGUF's (neurostream states its K-quant decode
+ *     is bit-exact against the reference gguf implementation): in Q4_K,
+ *     sub-block j < 4 takes scale = low 6 bits of scale byte j and min = low
+ *     6 bits of byte j + 4; j >= 4 takes scale = low nibble of byte j + 4 with
+ *     the top 2 bits of byte j - 4 above it, min = high nibble of byte j + 4
+ *     with the top 2 bits of byte j above it; nibble byte 32 c + l holds
+ *     element l of sub-block 2 c (low nibble) and of sub-block 2 c + 1 (high).
+ *     In Q6_K, element e = 128 h + 32 i + l (l < 32) takes the nibble
+ *     (i < 2 ? low : high) of low byte 64 h + 32 (i & 1) + l, bits 2 i, 2 i + 1
+ *     of high byte 32 h + l as its top two bits, and scale e / 16.
  *
- * Every decoded weight is exactly representable in fp32 for finite scales (an
- * fp16 has 11 significant bits, |q| <= 128 adds 8; E2M1 values have 2), so the
- * decoder returns fp32 and the dot product multiplies those fp32 values by the
- * fp32 x in fp64, where each product is exact.
+ * Every decoded weight of the 32-weight formats is exactly representable in
+ * fp32 for finite scales (an fp16 has 11 significant bits, |q| <= 128 adds 8;
+ * E2M1 values have 2).  K-quant weights are exact in fp64 and rounded once to
+ * fp32 (Q4_K: d sc q and dmin m are exact, their difference is not always;
+ * Q6_K: d scale (q - 32) can need 25 bits).  The decoder returns fp32 and the
+ * dot product multiplies those fp32 values by the fp32 x in fp64, where each
+ * product is exact.
  *
  * Threads split rows only; each row's sum is the same sequence of fp64
  * operations whatever the thread count.
@@ -54,6 +78,8 @@
 #define ORC_Q8_0 1
 #define ORC_Q4_0 2
 #define ORC_MXFP4 3
+#define ORC_Q4_K 4
+#define ORC_Q6_K 5
 
 #define ORC_OK 0
 #define ORC_EBAD (-1)
@@ -63,14 +89,22 @@ int64_t orc_block_bytes(int32_t fmt) {
     case ORC_Q8_0: return 2 + 32;   /* fp16 d + 32 x int8 */
     case ORC_Q4_0: return 2 + 16;   /* fp16 d + 32 nibbles */
     case ORC_MXFP4: return 1 + 16;  /* E8M0 e + 32 nibbles */
+    case ORC_Q4_K: return 2 + 2 + 12 + 128;  /* d, dmin, packed scales/mins, 256 nibbles */
+    case ORC_Q6_K: return 128 + 64 + 16 + 2; /* low nibbles, high bit pairs, scales, d */
     default: return ORC_EBAD;
   }
 }
 
+/* Weights per block. */
+int64_t orc_block_weights(int32_t fmt) {
+  if (orc_block_bytes(fmt) < 0) return ORC_EBAD;
+  return (fmt == ORC_Q4_K || fmt == ORC_Q6_K) ? 256 : 32;
+}
+
 int64_t orc_row_bytes(int32_t fmt, int64_t k) {
-  int64_t bb = orc_block_bytes(fmt);
-  if (bb < 0 || k <= 0 || k % 32 != 0) return ORC_EBAD;
-  return (k / 32) * bb;
+  int64_t bb = orc_block_bytes(fmt), qk = orc_block_weights(fmt);
+  if (bb < 0 || k <= 0 || k % qk != 0) return ORC_EBAD;
+  return (k / qk) * bb;
 }
 
 /* IEEE 754 binary16 -> double, from the bit fields (no host half type). */
@@ -108,9 +142,58 @@ static double e8m0_value(int e) {
   return ldexp(1.0, e - 127);
 }
 
-/* Decode one block into 32 fp32 weights, in element order. */
-static void decode_block(int32_t fmt, const uint8_t *b, float w[32]) {
-  if (fmt == ORC_Q8_0) {
+/* Q4_K's twelve scale bytes -> the 6-bit scale sc[j] and min m[j] of each
+ * sub-block j: the first four sub-blocks keep both fields whole in the low six
+ * bits of bytes 0..7; the last four keep their low four bits in the nibbles
+ * of bytes 8..11 and their top two bits in the spare top bits of bytes 0..7. */
+static void q4_k_scales_mins(const uint8_t s[12], int sc[8], int m[8]) {
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = s[j] & 63;
+    m[j] = s[j + 4] & 63;
+  }
+  for (int j = 4; j < 8; ++j) {
+    sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+    m[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+  }
+}
+
+/* One Q4_K super-block into 256 weights. */
+static void decode_q4_k(const uint8_t *b, float w[256]) {
+  double d = orc_half_to_double((uint16_t)(b[0] | (b[1] << 8)));
+  double dmin = orc_half_to_double((uint16_t)(b[2] | (b[3] << 8)));
+  int sc[8], m[8];
+  q4_k_scales_mins(b + 4, sc, m);
+  const uint8_t *qs = b + 16;
+  for (int j = 0; j < 8; ++j) {
+    for (int l = 0; l < 32; ++l) {
+      int byte = qs[32 * (j / 2) + l];
+      int q = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+      w[32 * j + l] = (float)(d * sc[j] * q - dmin * m[j]);
+    }
+  }
+}
+
+/* One Q6_K super-block into 256 weights. */
+static void decode_q6_k(const uint8_t *b, float w[256]) {
+  const uint8_t *ql = b, *qh = b + 128;
+  const int8_t *scale = (const int8_t *)(b + 192);
+  double d = orc_half_to_double((uint16_t)(b[208] | (b[209] << 8)));
+  for (int e = 0; e < 256; ++e) {
+    int h = e / 128, i = (e % 128) / 32, l = e % 32;
+    int low = (ql[64 * h + 32 * (i % 2) + l] >> (4 * (i / 2))) & 15;
+    int high = (qh[32 * h + l] >> (2 * i)) & 3;
+    int q = low | (high << 4);
+    w[e] = (float)(d * scale[e / 16] * (q - 32));
+  }
+}
+
+/* Decode one block into its 32 (or 256) fp32 weights, in element order. */
+static void decode_block(int32_t fmt, const uint8_t *b, float *w) {
+  if (fmt == ORC_Q4_K) {
+    decode_q4_k(b, w);
+  } else if (fmt == ORC_Q6_K) {
+    decode_q6_k(b, w);
+  } else if (fmt == ORC_Q8_0) {
     double d = orc_half_to_double((uint16_t)(b[0] | (b[1] << 8)));
     for (int j = 0; j < 32; ++j) w[j] = (float)(d * (double)(int8_t)b[2 + j]);
   } else if (fmt == ORC_Q4_0) {
@@ -142,10 +225,10 @@ static int check_args(int32_t fmt, int64_t n_rows, int64_t k, int64_t r0, int64_
 int orc_dequant_rows(int32_t fmt, const uint8_t *w, int64_t n_rows, int64_t k,
                      int64_t r0, int64_t r1, float *out) {
   if (check_args(fmt, n_rows, k, r0, r1) != ORC_OK) return ORC_EBAD;
-  int64_t bb = orc_block_bytes(fmt), rb = orc_row_bytes(fmt, k), nb = k / 32;
+  int64_t bb = orc_block_bytes(fmt), rb = orc_row_bytes(fmt, k), qk = orc_block_weights(fmt), nb = k / qk;
   for (int64_t r = r0; r < r1; ++r)
     for (int64_t b = 0; b < nb; ++b)
-      decode_block(fmt, w + r * rb + b * bb, out + (r - r0) * k + b * 32);
+      decode_block(fmt, w + r * rb + b * bb, out + (r - r0) * k + b * qk);
   return ORC_OK;
 }
 
@@ -153,13 +236,13 @@ int orc_dequant_rows(int32_t fmt, const uint8_t *w, int64_t n_rows, int64_t k,
  * scale a componentwise error bound is measured against). */
 static void gemv_row(int32_t fmt, const uint8_t *row, int64_t k, const float *x,
                      double *y, double *a) {
-  int64_t bb = orc_block_bytes(fmt), nb = k / 32;
-  float w[32];
+  int64_t bb = orc_block_bytes(fmt), qk = orc_block_weights(fmt), nb = k / qk;
+  float w[256];
   double acc = 0.0, aacc = 0.0;
   for (int64_t b = 0; b < nb; ++b) {
     decode_block(fmt, row + b * bb, w);
-    for (int j = 0; j < 32; ++j) {
-      double p = (double)w[j] * (double)x[b * 32 + j];
+    for (int j = 0; j < qk; ++j) {
+      double p = (double)w[j] * (double)x[b * qk + j];
       acc += p;
       aacc += fabs(p);
     }

@@ -14,6 +14,11 @@ Block layouts written here (byte order little-endian):
   Q8_0  (34 B): fp16 scale bits, then 32 int8 codes
   Q4_0  (18 B): fp16 scale bits, then 16 bytes of packed 4-bit codes
   MXFP4 (17 B): E8M0 scale byte, then 16 bytes of packed 4-bit codes
+and per 256-weight super-block:
+  Q4_K (144 B): fp16 d, fp16 dmin, 12 bytes of packed scales/mins, 128 bytes
+                of packed 4-bit codes
+  Q6_K (210 B): 128 bytes of low nibbles, 64 bytes of 2-bit high parts,
+                16 int8 scales, fp16 d
 """
 from __future__ import annotations
 
@@ -23,9 +28,10 @@ import subprocess
 
 import numpy as np
 
-Q8_0, Q4_0, MXFP4 = 1, 2, 3
-FMT_NAMES = {Q8_0: "q8_0", Q4_0: "q4_0", MXFP4: "mxfp4"}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
+Q8_0, Q4_0, MXFP4, Q4_K, Q6_K = 1, 2, 3, 4, 5
+FMT_NAMES = {Q8_0: "q8_0", Q4_0: "q4_0", MXFP4: "mxfp4", Q4_K: "q4_k", Q6_K: "q6_k"}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17, Q4_K: 144, Q6_K: 210}
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_0: 32, MXFP4: 32, Q4_K: 256, Q6_K: 256}
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -67,7 +73,13 @@ DEFAULTS = {
     Q8_0: dict(scale_lo=1e-3, scale_hi=1e-2, random_sign=True),
     Q4_0: dict(scale_lo=1e-3, scale_hi=1e-2, random_sign=False),
     MXFP4: dict(e_lo=118, e_hi=130),
+    Q4_K: dict(scale_lo=1e-4, scale_hi=1e-3, random_sign=False),
+    Q6_K: dict(scale_lo=1e-4, scale_hi=1e-3, random_sign=False),
 }
+
+
+def row_bytes(fmt: int, k: int) -> int:
+    return (k // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
 
 
 def blocks(fmt: int, n_rows: int, k: int, seed: int, r0: int = 0, r1: int | None = None, out=None,
@@ -79,14 +91,16 @@ def blocks(fmt: int, n_rows: int, k: int, seed: int, r0: int = 0, r1: int | None
       Q8_0 : d ~ fp16(U[1e-3, 1e-2)) * (+-1), q ~ U{-127..127}
       Q4_0 : d ~ fp16(U[1e-3, 1e-2)), every code byte ~ U{0..255}
       MXFP4: e ~ U{118..130}, every code byte ~ U{0..255}
+      Q4_K : d, dmin ~ fp16(U[1e-4, 1e-3)), scale/min and code bytes ~ U{0..255}
+      Q6_K : d ~ fp16(U[1e-4, 1e-3)), code bytes ~ U{0..255}, scales ~ U{-127..127}
     ``out`` (optional) is a C-contiguous uint8 array of the result's shape.
     """
-    assert k % 32 == 0 and k > 0
+    assert k % BLOCK_WEIGHTS[fmt] == 0 and k > 0
     r1 = n_rows if r1 is None else r1
     assert 0 <= r0 <= r1 <= n_rows
     q = dict(DEFAULTS[fmt])
     q.update(p)
-    rb = (k // 32) * BLOCK_BYTES[fmt]
+    rb = row_bytes(fmt, k)
     if out is None:
         out = np.empty((r1 - r0, rb), dtype=np.uint8)
     assert out.dtype == np.uint8 and out.flags.c_contiguous and out.size == (r1 - r0) * rb
@@ -115,7 +129,7 @@ def random_bytes(fmt: int, n_rows: int, k: int, seed: int) -> np.ndarray:
     """Blocks with every byte uniform (scales included): exercises every scale
     pattern, NaN/inf/subnormal scales among them, for the bit-exact decode checks."""
     g = rng(seed)
-    return g.integers(0, 256, size=(n_rows, (k // 32) * BLOCK_BYTES[fmt]), dtype=np.uint8)
+    return g.integers(0, 256, size=(n_rows, row_bytes(fmt, k)), dtype=np.uint8)
 
 
 def x_vec(k: int, seed: int) -> np.ndarray:

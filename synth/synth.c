@@ -18,6 +18,11 @@
  *          over {-127..127} (Lemire's multiply-shift on 32-bit words).
  *   Q4_0 : d as above; 16 code bytes uniform over 0..255.
  *   MXFP4: scale byte uniform over {e_lo..e_hi}; 16 code bytes uniform.
+ * and per 256-weight super-block:
+ *   Q4_K : d and dmin each as d above (dmin from its own stream, no sign);
+ *          the 12 scale/min bytes and 128 code bytes uniform over 0..255.
+ *   Q6_K : d as above (stored last); 192 low/high code bytes uniform over
+ *          0..255; 16 int8 scales uniform over {-127..127}.
  */
 #include <math.h>
 #include <pthread.h>
@@ -27,6 +32,8 @@
 #define SY_Q8_0 1
 #define SY_Q4_0 2
 #define SY_MXFP4 3
+#define SY_Q4_K 4
+#define SY_Q6_K 5
 
 static inline uint64_t sm64(uint64_t seed, uint64_t s, uint64_t i) {
   uint64_t z = seed + 0x9E3779B97F4A7C15ULL * (1 + ((s << 40) + i));
@@ -58,8 +65,42 @@ typedef struct {
   int32_t random_sign, e_lo, e_hi;
 } job_t;
 
+static uint16_t draw_half(const job_t *j, uint64_t s, uint64_t b) {
+  uint64_t r = sm64(j->seed, s, b);
+  double u = (double)(r >> 11) * 0x1.0p-53;
+  return synth_half_bits(j->lo + (j->hi - j->lo) * u);
+}
+
+static void put_half(uint8_t *p, uint16_t h) {
+  p[0] = (uint8_t)(h & 0xff);
+  p[1] = (uint8_t)(h >> 8);
+}
+
 static void fill_block(const job_t *j, uint64_t b, uint8_t *p) {
-  /* stream 0: scale, stream 1: codes */
+  /* stream 0: scale, stream 1: codes, stream 3: Q4_K's dmin, stream 4: Q6_K's scales */
+  if (j->fmt == SY_Q4_K) {
+    put_half(p, draw_half(j, 0, b));
+    put_half(p + 2, draw_half(j, 3, b));
+    for (int i = 0; i < 18; ++i) {  /* 140 bytes from 18 words */
+      uint64_t w = sm64(j->seed, 1, 18 * b + i);
+      int n = i < 17 ? 8 : 4;
+      memcpy(p + 4 + 8 * i, &w, (size_t)n);
+    }
+    return;
+  }
+  if (j->fmt == SY_Q6_K) {
+    for (int i = 0; i < 24; ++i) {  /* 192 code bytes */
+      uint64_t w = sm64(j->seed, 1, 24 * b + i);
+      memcpy(p + 8 * i, &w, 8);
+    }
+    for (int i = 0; i < 8; ++i) {
+      uint64_t w = sm64(j->seed, 4, 8 * b + i);
+      p[192 + 2 * i] = (uint8_t)(int8_t)((int)bounded((uint32_t)w, 255u) - 127);
+      p[193 + 2 * i] = (uint8_t)(int8_t)((int)bounded((uint32_t)(w >> 32), 255u) - 127);
+    }
+    put_half(p + 208, draw_half(j, 0, b));
+    return;
+  }
   if (j->fmt == SY_MXFP4) {
     uint32_t r = (uint32_t)sm64(j->seed, 0, b);
     p[0] = (uint8_t)(j->e_lo + bounded(r, (uint32_t)(j->e_hi - j->e_lo + 1)));
@@ -98,12 +139,14 @@ static void *worker(void *arg) {
 }
 
 /* Rows [r0, r1) of a seeded matrix of k inputs into out ((r1-r0) rows of
- * (k/32) blocks).  Returns 0, or -1 on bad arguments. */
+ * k/32 blocks, or k/256 super-blocks).  Returns 0, or -1 on bad arguments. */
 int synth_fill(int32_t fmt, uint8_t *out, int64_t k, int64_t r0, int64_t r1, uint64_t seed,
                double scale_lo, double scale_hi, int32_t random_sign, int32_t e_lo, int32_t e_hi,
                int32_t nthreads) {
-  int64_t bb = fmt == SY_Q8_0 ? 34 : fmt == SY_Q4_0 ? 18 : fmt == SY_MXFP4 ? 17 : -1;
-  if (bb < 0 || k <= 0 || k % 32 || r0 < 0 || r1 < r0) return -1;
+  int64_t bb = fmt == SY_Q8_0 ? 34 : fmt == SY_Q4_0 ? 18 : fmt == SY_MXFP4 ? 17
+             : fmt == SY_Q4_K ? 144 : fmt == SY_Q6_K ? 210 : -1;
+  int64_t qk = (fmt == SY_Q4_K || fmt == SY_Q6_K) ? 256 : 32;
+  if (bb < 0 || k <= 0 || k % qk || r0 < 0 || r1 < r0) return -1;
   if (fmt != SY_MXFP4 && !(scale_lo > 6.2e-5 && scale_hi > scale_lo && scale_hi < 65504.0)) return -1;
   if (fmt == SY_MXFP4 && !(0 <= e_lo && e_lo <= e_hi && e_hi <= 255)) return -1;
   if (nthreads < 1) nthreads = 1;
@@ -114,7 +157,7 @@ int synth_fill(int32_t fmt, uint8_t *out, int64_t k, int64_t r0, int64_t r1, uin
   job_t jobs[64];
   pthread_t th[64];
   for (int t = 0; t < nthreads; ++t) {
-    job_t j = {fmt, out, k / 32, bb, r0, r0 + n * t / nthreads, r0 + n * (t + 1) / nthreads,
+    job_t j = {fmt, out, k / qk, bb, r0, r0 + n * t / nthreads, r0 + n * (t + 1) / nthreads,
                seed, scale_lo, scale_hi, random_sign, e_lo, e_hi};
     jobs[t] = j;
   }

@@ -33,7 +33,7 @@ MUTANTS = [
     ("e2m1_subnormal", "double v = (e == 0) ? 0.5 * m", "double v = (e == 0) ? 1.0 * m"),
     ("e2m1_sign_bit", "int s = (code >> 3) & 1;", "int s = (code >> 2) & 1;"),
     ("mxfp4_scale_last", "double s = e8m0_value(b[0]);", "double s = e8m0_value(b[16]);"),
-    ("x_transposed", "(double)x[b * 32 + j]", "(double)x[j * nb + b]"),
+    ("x_transposed", "(double)x[b * qk + j]", "(double)x[j * nb + b]"),
     ("last_block_dropped", "for (int64_t b = 0; b < nb; ++b) {\n    decode_block(fmt, row + b * bb, w);",
      "for (int64_t b = 0; b + 1 < nb; ++b) {\n    decode_block(fmt, row + b * bb, w);"),
     ("window_offset_lost", "gemv_row(j->fmt, j->w + r * j->rb", "gemv_row(j->fmt, j->w + (r - j->r0) * j->rb"),
@@ -42,6 +42,26 @@ MUTANTS = [
     ("rms_mean_dropped", "1.0 / sqrt(ss / (double)n + eps)", "1.0 / sqrt(ss + eps)"),
     ("gelu_scale", "erfc(-v[i] / sqrt(2.0))", "erfc(-v[i])"),
     ("gelu_cancelling", "0.5 * v[i] * erfc(-v[i] / sqrt(2.0))", "0.5 * v[i] * (1.0 + erf(v[i] / sqrt(2.0)))"),
+    ("q4k_min_added", "w[32 * j + l] = (float)(d * sc[j] * q - dmin * m[j]);",
+     "w[32 * j + l] = (float)(d * sc[j] * q + dmin * m[j]);"),
+    ("q4k_dmin_is_d", "double dmin = orc_half_to_double((uint16_t)(b[2] | (b[3] << 8)));",
+     "double dmin = orc_half_to_double((uint16_t)(b[0] | (b[1] << 8)));"),
+    ("q4k_scale_min_swapped", "sc[j] = s[j] & 63;\n    m[j] = s[j + 4] & 63;",
+     "sc[j] = s[j + 4] & 63;\n    m[j] = s[j] & 63;"),
+    ("q4k_top_bits_wrong_byte", "sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);",
+     "sc[j] = (s[j + 4] & 15) | ((s[j] >> 6) << 4);"),
+    ("q4k_nibble_parity", "int q = (j % 2 == 0) ? (byte & 15) : (byte >> 4);",
+     "int q = (j % 2 == 1) ? (byte & 15) : (byte >> 4);"),
+    ("q4k_code_stride", "int byte = qs[32 * (j / 2) + l];", "int byte = qs[32 * (j % 4) + l];"),
+    ("q6k_offset_31", "w[e] = (float)(d * scale[e / 16] * (q - 32));", "w[e] = (float)(d * scale[e / 16] * (q - 31));"),
+    ("q6k_scale_per_32", "w[e] = (float)(d * scale[e / 16] * (q - 32));", "w[e] = (float)(d * scale[e / 32] * (q - 32));"),
+    ("q6k_high_shift", "int high = (qh[32 * h + l] >> (2 * i)) & 3;", "int high = (qh[32 * h + l] >> i) & 3;"),
+    ("q6k_low_select", "int low = (ql[64 * h + 32 * (i % 2) + l] >> (4 * (i / 2))) & 15;",
+     "int low = (ql[64 * h + 32 * (i / 2) + l] >> (4 * (i % 2))) & 15;"),
+    ("q6k_d_first", "double d = orc_half_to_double((uint16_t)(b[208] | (b[209] << 8)));",
+     "double d = orc_half_to_double((uint16_t)(b[0] | (b[1] << 8)));"),
+    ("q6k_unsigned_scale", "const int8_t *scale = (const int8_t *)(b + 192);", "const uint8_t *scale = b + 192;"),
+    ("kquant_block_weights_32", "return (fmt == ORC_Q4_K || fmt == ORC_Q6_K) ? 256 : 32;", "return 32;"),
 ]
 
 # pins, cheapest first; a mutant is caught at the first one that fails
@@ -60,6 +80,13 @@ PINS = [
     pins.test_q4_0_every_code_at_every_position,
     pins.test_fp16_all_65536_patterns_match_struct,
     pins.test_q8_0_bruteforce_every_scale_and_code,
+    pins.test_q4_k_field_order_and_formula,
+    pins.test_q4_k_scale_field_is_a_bijection,
+    pins.test_q4_k_codes_are_a_bijection,
+    pins.test_q4_k_hand_built_blocks,
+    pins.test_q6_k_codes_are_a_bijection_and_centered,
+    pins.test_q6_k_scales_cover_runs_of_16,
+    pins.test_q6_k_hand_built_blocks,
 ]
 
 PARAMS = {
