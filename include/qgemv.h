@@ -1,12 +1,13 @@
 /*
  * qgemv.h -- C ABI of libqgemv.so: batch-1 dequant-GEMV over GGUF
- * block-quantized weights (Q8_0, Q4_0, MXFP4) on an AMD Instinct MI355X
- * (gfx950).
+ * block-quantized weights (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K) on an AMD Instinct
+ * MI355X (gfx950).
  *
  * The operation (RAMforge README, "Milestone 6 - True Out-of-Core Integrity",
  * matrix layout): a weight matrix of n_rows output rows and k inputs is stored
- * row-major, [n_rows][k/32 blocks], each row a whole number of 32-weight quant
- * blocks (neurostream README, "The idea"), and
+ * row-major, [n_rows][k/QK blocks], each row a whole number of quant blocks
+ * (neurostream README, "The idea"; QK = 32 weights per block, 256 for the
+ * K-quant super-blocks), and
  *
  *     y[j] = sum_{i<k} W[row_start + j, i] * x[i],   0 <= j < row_end - row_start
  *
@@ -22,6 +23,24 @@
  * Nibble order: element j < 16 is the low nibble of qs[j], element j + 16 the
  * high nibble (the GGUF split-half order).  E2M1 is the OCP MX 4-bit float
  * (sign bit 3, two exponent bits with bias 1, one mantissa bit); e = 255 is NaN.
+ *
+ * K-quants: 256-weight super-blocks of eight 32-weight sub-blocks, in GGUF's
+ * byte layout (neurostream README, "Supported": Q4_K and Q6_K decode
+ * bit-exact against the reference gguf implementation):
+ *   QG_Q4_K 144 B: fp16 d, fp16 dmin, uint8 scales[12], uint8 qs[128];
+ *                  w = d * sc_s * q - dmin * m_s, sub-block s of 32 weights
+ *                  (RAMforge README, "Milestone 5", Q4_K line).  scales[]
+ *                  packs eight 6-bit sc and eight 6-bit m: s < 4 keeps
+ *                  sc_s = scales[s] & 63, m_s = scales[s+4] & 63; s >= 4 keeps
+ *                  their low nibbles in scales[s+4] (sc low, m high) and their
+ *                  top two bits in the top bits of scales[s-4] (sc) and
+ *                  scales[s] (m).  qs[32c + l] holds element l of sub-block 2c
+ *                  (low nibble) and of sub-block 2c + 1 (high nibble).
+ *   QG_Q6_K 210 B: uint8 ql[128], uint8 qh[64], int8 scales[16], fp16 d;
+ *                  w_e = d * scales[e/16] * (q_e - 32) with the 6-bit code of
+ *                  element e = 128h + 32i + l (l < 32): low four bits from
+ *                  ql[64h + 32(i&1) + l] (low nibble for i < 2, else high),
+ *                  top two bits from bits 2i, 2i+1 of qh[32h + l].
  *
  * Conventions shared by every entry point
  *  - Status: 0 (QG_OK) or a negative qg_status.  Arguments are validated on the
@@ -53,18 +72,18 @@ extern "C" {
 /* Same type as HIP's hipStream_t. */
 typedef struct ihipStream_t *qg_stream_t;
 
-enum qg_format { QG_Q8_0 = 1, QG_Q4_0 = 2, QG_MXFP4 = 3 };
+enum qg_format { QG_Q8_0 = 1, QG_Q4_0 = 2, QG_MXFP4 = 3, QG_Q4_K = 4, QG_Q6_K = 5 };
 
 enum qg_status {
   QG_OK = 0,
   QG_E_NULL = -1,       /* a required pointer is NULL */
   QG_E_FMT = -2,        /* unknown format (RAMforge README, "Capability registry":
                            unsupported types are an explicit error) */
-  QG_E_SHAPE = -3,      /* k <= 0, k % 32 != 0, k > QG_MAX_K, n_rows < 0,
+  QG_E_SHAPE = -3,      /* k <= 0, k % QK != 0, k > QG_MAX_K, n_rows < 0,
                            n_expert <= 0, rows not a multiple of n_expert */
   QG_E_RANGE = -4,      /* row_start < 0, row_start > row_end, row_end > n_rows,
                            expert id outside [0, n_expert) */
-  QG_E_SIZE = -5,       /* n_bytes != n_rows * (k/32) * block bytes (truncated or
+  QG_E_SIZE = -5,       /* n_bytes != n_rows * (k/QK) * block bytes (truncated or
                            oversized tensors are rejected: RAMforge README,
                            "Build & Test", quant.rs unit tests) */
   QG_E_ARG = -6,        /* block_rows < 0, lookahead < 1, n_win < 0 or above
@@ -90,14 +109,14 @@ enum qg_status {
  * quantized tensor (RAMforge README, "Milestone 5", QuantizedTensor: raw block
  * bytes plus type and shape). */
 typedef struct qg_matrix {
-  const void *data; /* n_bytes of blocks, row-major [n_rows][k/32]; 16-byte
+  const void *data; /* n_bytes of blocks, row-major [n_rows][k/QK]; 16-byte
                        aligned.  Kernels fetch whole aligned 16-byte granules,
                        so they may read up to 15 bytes past the last row
                        inside the granule holding its last byte. */
   int32_t fmt;      /* enum qg_format */
   int32_t reserved; /* must be 0 */
   int64_t n_rows;   /* output rows */
-  int64_t k;        /* inputs per row, a multiple of 32 */
+  int64_t k;        /* inputs per row, a multiple of 32 (256 for K-quants) */
   int64_t n_bytes;  /* must equal qgemv_weight_bytes(fmt, n_rows, k) */
 } qg_matrix;
 
@@ -113,8 +132,12 @@ typedef struct qg_window {
   float *y;          /* device, row_end - row_start values: y[j] <-> row row_start + j */
 } qg_window;
 
-/* Bytes per 32-weight block: 34, 18 or 17; QG_E_FMT for an unknown format. */
+/* Bytes per block: 34, 18, 17, 144 or 210; QG_E_FMT for an unknown format. */
 int64_t qgemv_block_bytes(int32_t fmt);
+
+/* Weights per block (QK): 32, or 256 for Q4_K and Q6_K; QG_E_FMT for an
+ * unknown format. */
+int64_t qgemv_block_weights(int32_t fmt);
 
 /* Bytes of an n_rows x k matrix, or a negative status (QG_E_FMT, QG_E_SHAPE). */
 int64_t qgemv_weight_bytes(int32_t fmt, int64_t n_rows, int64_t k);
@@ -287,7 +310,8 @@ typedef struct qg_chain_step {
 typedef struct qg_chain qg_chain;
 
 /* Validates and uploads a chain of n_steps steps over the host arrays steps
- * and win (all windows of one fmt), sized for the current device.  The chain
+ * and win (all windows of one fmt: Q8_0, Q4_0 or MXFP4; a K-quant format
+ * returns QG_E_FMT), sized for the current device.  The chain
  * keeps the pointers, not the data: every buffer must outlive its runs.
  * Within a step, a window's y must not overlap any x, x2 or other y of that
  * step, and no step may write weights.  Synchronising. */

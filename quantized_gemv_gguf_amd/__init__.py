@@ -1,5 +1,5 @@
 """Python binding of libqgemv.so (include/qgemv.h): batch-1 dequant-GEMV over
-GGUF block-quantized weights (Q8_0, Q4_0, MXFP4) on MI355X.
+GGUF block-quantized weights (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K) on MI355X.
 
 The functions carry the C names and do argument marshalling only: torch
 tensors are turned into raw pointers and sizes, the caller's torch stream into
@@ -14,8 +14,8 @@ import os
 from dataclasses import dataclass
 from typing import Sequence
 
-Q8_0, Q4_0, MXFP4 = 1, 2, 3
-FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "mxfp4": MXFP4}
+Q8_0, Q4_0, MXFP4, Q4_K, Q6_K = 1, 2, 3, 4, 5
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "mxfp4": MXFP4, "q4_k": Q4_K, "q6_k": Q6_K}
 MAX_WINDOWS = 64
 MAX_K = 49152
 CHAIN_MAX_K = 24576
@@ -78,6 +78,7 @@ def lib():
     P = ctypes.POINTER
     sigs = {
         "qgemv_block_bytes": ([_i32], _i64),
+        "qgemv_block_weights": ([_i32], _i64),
         "qgemv_weight_bytes": ([_i32, _i64, _i64], _i64),
         "qgemv_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
@@ -191,6 +192,10 @@ def _windows(ws: Sequence[Window]):
 
 def qgemv_block_bytes(fmt: int) -> int:
     return int(lib().qgemv_block_bytes(fmt))
+
+
+def qgemv_block_weights(fmt: int) -> int:
+    return int(lib().qgemv_block_weights(fmt))
 
 
 def qgemv_weight_bytes(fmt: int, n_rows: int, k: int) -> int:

@@ -3,7 +3,7 @@
 // (block formats, fused row dot, LDS-DMA weight ring) lives in qgemv_impl.h,
 // instantiated per fused-transform variant in gemv_op*.hip.
 //
-// Batch-1 dequant-GEMV over GGUF blocks (Q8_0, Q4_0, MXFP4): every output row
+// Batch-1 dequant-GEMV over GGUF blocks (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K): every output row
 // is a dot product of its dequantized weights with an fp32 activation vector,
 // accumulated in fp32, the weights decoded in registers and never written out
 // (neurostream README, "How it works", step 5: the fused decode-path GEMV).
@@ -16,7 +16,8 @@
 //   A "team" is one workgroup of WT wavefronts (T = 64 * WT lanes).  Team lane
 //   t owns the block columns j = t + T*c (c < C) of every row it touches, and
 //   keeps the 32 activations of each such column in registers, loaded once per
-//   window.  A row is one pass: each lane dots its C blocks (32 weights each),
+//   window (a "column" is 32 weights: a block, or a K-quant sub-block).  A row
+//   is one pass: each lane dots its C columns,
 //   the 64 lanes of a wave are combined by fixed DPP shifts, and for
 //   WT > 1 the per-wave sums go through LDS and are added in wave order.
 //   (WT, C) is a function of (format, k) only, and so is the whole per-row
@@ -27,7 +28,7 @@
 //   tiles of all windows are numbered in window order, and team b takes tiles
 //   b, b + T, b + 2T, ... (T teams in the grid).
 //
-// Matrix layout: row-major [n_rows][k/32 blocks], y[o] = sum_i W[o, i] x[i]
+// Matrix layout: row-major [n_rows][k/QK blocks], y[o] = sum_i W[o, i] x[i]
 // (RAMforge README, "Milestone 6", matrix layout).  Each row is a whole number
 // of blocks, so a row window is one contiguous byte range (neurostream README,
 // "The idea").
@@ -64,6 +65,7 @@ namespace {
 // Dequant (test aid), SiLU*up, RMS carry
 // ---------------------------------------------------------------------------
 
+// One thread per 32 weights (nb of them per row).
 template <int FMT>
 __global__ void dequant_kernel(const uint8_t *base, int64_t row_start, int64_t n_rows, int nb,
                                int64_t row_bytes, float *out) {
@@ -72,6 +74,15 @@ __global__ void dequant_kernel(const uint8_t *base, int64_t row_start, int64_t n
   if (id >= n_rows * nb) return;
   const int64_t r = id / nb;
   const int j = (int)(id - r * nb);
+  if constexpr (F::kUnits > 1) {
+    const uint8_t *blk = base + (row_start + r) * row_bytes + (int64_t)F::kBytes * (j / F::kUnits);
+    float w[32];
+    F::dequant(blk, j % F::kUnits, w);
+    float *o = out + r * (int64_t)nb * 32 + 32 * j;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[e] = w[e];
+    return;
+  } else {
   const uint8_t *p = base + (row_start + r) * row_bytes + (int64_t)F::kBytes * j;
   uint32_t sbits = 0, q[F::kWords];
   __builtin_memcpy(&sbits, p, F::kScaleBytes);
@@ -82,6 +93,7 @@ __global__ void dequant_kernel(const uint8_t *base, int64_t row_start, int64_t n
   float *o = out + r * (int64_t)nb * 32 + 32 * j;
 #pragma unroll
   for (int e = 0; e < 32; ++e) o[e] = F::apply(s, u[e]);
+  }
 }
 
 __global__ void silu_mul_kernel(const float *g, const float *u, float *h, int64_t n) {
@@ -659,7 +671,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         if (i < nrows) {
           __builtin_amdgcn_wave_barrier();
           const int ph = (int)((uintptr_t)(done.row0 + (uint32_t)i * done.rb) & 15);
-          const float sp = row_partial<FMT, C>(sb, ph, lane, done.slice_n, xr);
+          const float sp = row_partial<FMT, C>(sb, ph, lane, done.slice_n, xr, kNoSums<C>);
           acc[i] = wave_sum63(sp);
           __builtin_amdgcn_wave_barrier();
         }
@@ -741,22 +753,33 @@ int block_bytes(int32_t fmt) {
     case QG_Q8_0: return Fmt<QG_Q8_0>::kBytes;
     case QG_Q4_0: return Fmt<QG_Q4_0>::kBytes;
     case QG_MXFP4: return Fmt<QG_MXFP4>::kBytes;
+    case QG_Q4_K: return Fmt<QG_Q4_K>::kBytes;
+    case QG_Q6_K: return Fmt<QG_Q6_K>::kBytes;
     default: return QG_E_FMT;
   }
 }
 
+bool kquant(int32_t fmt) { return fmt == QG_Q4_K || fmt == QG_Q6_K; }
+
+// Weights per block.
+int block_weights(int32_t fmt) { return block_bytes(fmt) < 0 ? QG_E_FMT : kquant(fmt) ? 256 : 32; }
+
+// Bytes of one row of k inputs (fmt and k already checked).
+int64_t row_bytes_of(int32_t fmt, int64_t k) { return k / block_weights(fmt) * block_bytes(fmt); }
+
 int check_fmt_k(int32_t fmt, int64_t k) {
   if (block_bytes(fmt) < 0) return QG_E_FMT;
-  if (k <= 0 || k % 32 != 0) return QG_E_SHAPE;
+  if (k <= 0 || k % block_weights(fmt) != 0) return QG_E_SHAPE;
   return QG_OK;
 }
 
-// Team shape, a function of (format, k) only.  Q8_0: one block column per
-// lane while a row fits 12 waves (k <= 24576), else two.  Q4_0 and MXFP4: two
-// columns per lane: their decode is VALU-bound, and a lane's second block
-// shares the row's staging, reduction and addressing work.  The team has
-// one wave per 64*C columns, so every wave owns at least one block.
-int first_c(int32_t fmt) { return fmt == QG_Q8_0 ? 1 : 2; }
+// Team shape, a function of (format, k) only.  Q8_0 and the K-quants: one
+// column per lane while a row fits 12 waves (k <= 24576), else two.  Q4_0 and
+// MXFP4: two columns per lane: their decode is VALU-bound, and a lane's second
+// block shares the row's staging, reduction and addressing work.  The team
+// has one wave per 64*C columns, so every wave owns at least one column (and,
+// for the K-quants, whole super-blocks: k is a multiple of 256).
+int first_c(int32_t fmt) { return fmt == QG_Q8_0 || kquant(fmt) ? 1 : 2; }
 
 int team_shape(int32_t fmt, int64_t k, Shape *s) {
   const int64_t nb = k / 32;
@@ -782,7 +805,7 @@ int check_matrix(const qg_matrix *w) {
   if (w->n_rows < 0 || w->reserved != 0) return w->n_rows < 0 ? QG_E_SHAPE : QG_E_ARG;
   Shape s;
   if ((rc = team_shape(w->fmt, w->k, &s))) return rc;
-  if (w->n_bytes != w->n_rows * (w->k / 32) * block_bytes(w->fmt)) return QG_E_SIZE;
+  if (w->n_bytes != w->n_rows * row_bytes_of(w->fmt, w->k)) return QG_E_SIZE;
   if (!w->data && w->n_bytes > 0) return QG_E_NULL;
   if ((uintptr_t)w->data & 15) return QG_E_ARG;
   return QG_OK;
@@ -862,7 +885,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   for (int i = n; i <= kMaxWindows; ++i) a.tile_prefix[i] = (int32_t)tiles;
   a.n_win = n;
   a.nb = (int32_t)(k / 32);
-  a.row_bytes = (k / 32) * block_bytes(fmt);
+  a.row_bytes = row_bytes_of(fmt, k);
   a.block_rows = B;
   a.tile_rows = tile_rows;
   a.n_tiles = (int32_t)tiles;
@@ -920,9 +943,9 @@ const char *qgemv_strerror(int status) {
     case QG_OK: return "ok";
     case QG_E_NULL: return "a required pointer is NULL";
     case QG_E_FMT: return "unknown quantization format";
-    case QG_E_SHAPE: return "bad shape (k must be a positive multiple of 32, at most 49152; n_rows >= 0)";
+    case QG_E_SHAPE: return "bad shape (k must be a positive multiple of 32 (256 for K-quants), at most 49152; n_rows >= 0)";
     case QG_E_RANGE: return "row range or expert id out of range";
-    case QG_E_SIZE: return "n_bytes does not match n_rows * (k/32) * block bytes";
+    case QG_E_SIZE: return "n_bytes does not match n_rows * (k/QK) * block bytes";
     case QG_E_ARG: return "bad argument (block_rows, lookahead, window count, n, eps, stride, or weights not 16-byte aligned)";
     case QG_E_NOT_PINNED: return "streamed weights are not in page-locked host memory";
     case QG_E_CAPACITY: return "a row block is larger than a ring slot";
@@ -936,11 +959,13 @@ const char *qgemv_last_hip_error(void) { return g_last_hip.c_str(); }
 
 int64_t qgemv_block_bytes(int32_t fmt) { return block_bytes(fmt); }
 
+int64_t qgemv_block_weights(int32_t fmt) { return block_weights(fmt); }
+
 int64_t qgemv_weight_bytes(int32_t fmt, int64_t n_rows, int64_t k) {
   int rc = check_fmt_k(fmt, k);
   if (rc) return rc;
   if (n_rows < 0) return QG_E_SHAPE;
-  return n_rows * (k / 32) * block_bytes(fmt);
+  return n_rows * row_bytes_of(fmt, k);
 }
 
 int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, float *y,
@@ -1039,7 +1064,7 @@ int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, f
   if (row_end == row_start) return QG_OK;
   if (!out) return QG_E_NULL;
   const int nb = (int)(w->k / 32);
-  const int64_t rb = (w->k / 32) * block_bytes(w->fmt);
+  const int64_t rb = row_bytes_of(w->fmt, w->k);
   const int64_t n = (row_end - row_start) * nb;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   const uint8_t *base = (const uint8_t *)w->data;
@@ -1050,6 +1075,14 @@ int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, f
       break;
     case QG_Q4_0:
       hipLaunchKernelGGL(dequant_kernel<QG_Q4_0>, dim3(blocks), dim3(256), 0, stream, base, row_start,
+                         row_end - row_start, nb, rb, out);
+      break;
+    case QG_Q4_K:
+      hipLaunchKernelGGL(dequant_kernel<QG_Q4_K>, dim3(blocks), dim3(256), 0, stream, base, row_start,
+                         row_end - row_start, nb, rb, out);
+      break;
+    case QG_Q6_K:
+      hipLaunchKernelGGL(dequant_kernel<QG_Q6_K>, dim3(blocks), dim3(256), 0, stream, base, row_start,
                          row_end - row_start, nb, rb, out);
       break;
     default:
@@ -1155,7 +1188,7 @@ int mapped_alias(const void *host, const void **dev) {
 // Stream the row blocks of validated windows through the ring.
 int stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win, int n_win,
                    int64_t block_rows, hipStream_t stream) {
-  const int64_t rb = (k / 32) * block_bytes(fmt);
+  const int64_t rb = row_bytes_of(fmt, k);
   const int nslot = st->lookahead + 1;
   // every block must fit a slot; check all before enqueueing anything
   for (int i = 0; i < n_win; ++i) {
@@ -1278,7 +1311,7 @@ bool rms_op(int32_t op) { return op == QG_IN_RMS || op == QG_IN_GELU_RMS; }
 int validate_chain(int32_t fmt, const qg_chain_step *steps, int32_t n_steps, const qg_chain_window *win,
                    int32_t n_win) {
   if (!steps || !win) return QG_E_NULL;
-  if (block_bytes(fmt) < 0) return QG_E_FMT;
+  if (block_bytes(fmt) < 0 || kquant(fmt)) return QG_E_FMT;  // no K-quant chain kernel
   if (n_steps < 1 || n_win < 1) return QG_E_ARG;
   for (int i = 0; i < n_win; ++i) {
     if (win[i].n_rows < 0) return QG_E_SHAPE;

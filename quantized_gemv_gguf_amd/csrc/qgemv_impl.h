@@ -24,19 +24,22 @@ constexpr int kMaxC = 2;         // block columns per lane
 constexpr int kMaxWT = 12;       // waves per team
 
 // ---------------------------------------------------------------------------
-// Formats.  A block is a scale field followed by a payload of kWords 32-bit
-// words.  decode() turns the payload into 32 "unit" values u_j and scale()
-// the scale field into a Scale such that the weight is w_j = apply(scale, u_j);
-// the GEMV applies the scale once to a block's partial dot product, the
-// dequant kernel applies it to every u_j.  Both use the same decoder, so the
-// bit-exact decode check covers the GEMV's decoder.
+// Formats.  The unit of work of a lane is 32 consecutive weights: a whole
+// block of the 32-weight formats, one sub-block (kUnits = 8 per block) of the
+// 256-weight K-quant super-blocks.  A 32-weight block is a scale field
+// followed by a payload of kWords 32-bit words.  decode() turns the payload
+// into 32 "unit" values u_j and scale() the scale field into a Scale such that
+// the weight is w_j = apply(scale, u_j); the GEMV applies the scale once to a
+// block's partial dot product, the dequant kernel applies it to every u_j.
+// Both use the same decoder, so the bit-exact decode check covers the GEMV's
+// decoder.
 // ---------------------------------------------------------------------------
 
 template <int FMT> struct Fmt;
 
 // Q8_0: fp16 d, 32 x int8 q; w = d * q (RAMforge README, "Milestone 5").
 template <> struct Fmt<QG_Q8_0> {
-  static constexpr int kBytes = 34, kScaleBytes = 2, kWords = 8;
+  static constexpr int kBytes = 34, kScaleBytes = 2, kWords = 8, kUnits = 1;
   struct Scale { float d; };
   __device__ static inline Scale scale(uint32_t bits) {
     return Scale{__half2float(__ushort_as_half((uint16_t)bits))};
@@ -58,7 +61,7 @@ template <> struct Fmt<QG_Q8_0> {
 // top of a byte it reads as the int8 16 * (q - 8), exactly, and the 1/16 goes
 // into the scale (a power of two, so d/16 is exact too).
 template <> struct Fmt<QG_Q4_0> {
-  static constexpr int kBytes = 18, kScaleBytes = 2, kWords = 4;
+  static constexpr int kBytes = 18, kScaleBytes = 2, kWords = 4, kUnits = 1;
   struct Scale { float d16; };
   __device__ static inline Scale scale(uint32_t bits) {
     return Scale{__half2float(__ushort_as_half((uint16_t)bits)) * 0.0625f};
@@ -86,7 +89,7 @@ template <> struct Fmt<QG_Q4_0> {
 // (scale 1.0: the E2M1 value itself, exact); the E8M0 scale is applied with an
 // exact ldexp, and e = 255 gives NaN.
 template <> struct Fmt<QG_MXFP4> {
-  static constexpr int kBytes = 17, kScaleBytes = 1, kWords = 4;
+  static constexpr int kBytes = 17, kScaleBytes = 1, kWords = 4, kUnits = 1;
   struct Scale { int e; };
   __device__ static inline Scale scale(uint32_t bits) { return Scale{(int)(bits & 0xffu)}; }
   // f = (value of the byte's low nibble, value of its high nibble)
@@ -108,6 +111,116 @@ template <> struct Fmt<QG_MXFP4> {
     return s.e == 255 ? __builtin_nanf("") : ldexpf(v, s.e - 127);
   }
   __device__ static inline float fma_acc(Scale s, float v, float acc) { return acc + apply(s, v); }
+};
+
+__device__ __forceinline__ float half_bits(uint32_t h) { return __half2float(__ushort_as_half((uint16_t)h)); }
+
+// Q4_K: 144-byte super-block of 256 weights = fp16 d, fp16 dmin, 12 bytes of
+// packed 6-bit sub-block scales sc and mins m, 128 bytes of nibbles;
+// w = d sc q - dmin m (RAMforge README, "Milestone 5", Q4_K line), in GGUF's
+// packing: sub-block s < 4 keeps sc and m in the low six bits of scale bytes
+// s and s + 4; s >= 4 keeps their low nibbles in byte s + 4 and their top two
+// bits in the top bits of bytes s - 4 (sc) and s (m).  The codes of
+// sub-block s are one nibble (low for even s) of bytes 32 (s / 2) .. + 31.
+// A unit's dot is d sc (sum q x) - dmin m (sum x), with sum x formed once per
+// activation vector.
+template <> struct Fmt<QG_Q4_K> {
+  static constexpr int kBytes = 144, kUnits = 8;
+  __device__ static inline void scale_min(const uint8_t *blk, int s, int &sc, int &m) {
+    const int a = blk[4 + (s & 3)], b = blk[8 + (s & 3)], c = blk[12 + (s & 3)];
+    sc = s < 4 ? (a & 63) : ((c & 15) | ((a >> 6) << 4));
+    m = s < 4 ? (b & 63) : ((c >> 4) | ((b >> 6) << 4));
+  }
+  template <typename P>
+  __device__ static inline void codes(const P *blk, int s, uint32_t q[8]) {
+    __builtin_memcpy(q, blk + 16 + 32 * (s >> 1), 32);
+    const int sh = 4 * (s & 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (q[i] >> sh) & 0x0F0F0F0Fu;
+  }
+  __device__ static inline float dot(const uint8_t *blk, int s, const float (&x)[32], const float (&xs)[2],
+                                     float acc) {
+    uint32_t hd;
+    __builtin_memcpy(&hd, blk, 4);
+    int sc, m;
+    scale_min(blk, s, sc, m);
+    uint32_t q[8];
+    codes(blk, s, q);
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p[k] = fmaf((float)((q[i] >> (8 * k)) & 0xffu), x[4 * i + k], p[k]);
+    acc = fmaf(half_bits(hd) * (float)sc, (p[0] + p[1]) + (p[2] + p[3]), acc);
+    return fmaf(-(half_bits(hd >> 16) * (float)m), xs[0] + xs[1], acc);
+  }
+  // The 32 weights of sub-block s, each rounded once: d sc q and dmin m are
+  // exact in fp32.
+  __device__ static inline void dequant(const uint8_t *blk, int s, float w[32]) {
+    uint32_t hd;
+    __builtin_memcpy(&hd, blk, 4);
+    int sc, m;
+    scale_min(blk, s, sc, m);
+    uint32_t q[8];
+    codes(blk, s, q);
+    const float ds = half_bits(hd) * (float)sc, mm = half_bits(hd >> 16) * (float)m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[4 * i + k] = ds * (float)((q[i] >> (8 * k)) & 0xffu) - mm;
+  }
+};
+
+// Q6_K: 210-byte super-block of 256 weights = 128 bytes of low nibbles ql,
+// 64 bytes of 2-bit high parts qh, 16 int8 scales (one per 16 weights), fp16
+// d; w = d scale (q - 32) (GGUF's layout; the pages name the format only).
+// Unit u = 4 h + i (32 weights 128 h + 32 i + l) takes its low nibbles from
+// ql[64 h + 32 (i & 1) + l] (high nibble for i >= 2), its top bits from bits
+// 2 i, 2 i + 1 of qh[32 h + l], its scales from bytes 2 u, 2 u + 1.  A unit's
+// dot is d (scale_a (sum q x - 32 sum x) + scale_b (...)) over its halves,
+// with the half sums of x formed once per activation vector.
+template <> struct Fmt<QG_Q6_K> {
+  static constexpr int kBytes = 210, kUnits = 8;
+  template <typename P>
+  __device__ static inline void codes(const P *blk, int u, uint32_t q[8]) {
+    const int h = u >> 2, i = u & 3;
+    uint32_t lo[8], hi[8];
+    __builtin_memcpy(lo, blk + 64 * h + 32 * (i & 1), 32);
+    __builtin_memcpy(hi, blk + 128 + 32 * h, 32);
+    const int s4 = 4 * (i >> 1), s2 = 2 * i;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) q[w] = ((lo[w] >> s4) & 0x0F0F0F0Fu) | (((hi[w] >> s2) & 0x03030303u) << 4);
+  }
+  __device__ static inline float dot(const uint8_t *blk, int u, const float (&x)[32], const float (&xs)[2],
+                                     float acc) {
+    uint32_t q[8];
+    codes(blk, u, q);
+    const float sa = (float)(int8_t)blk[192 + 2 * u], sb = (float)(int8_t)blk[193 + 2 * u];
+    uint32_t hd = 0;
+    __builtin_memcpy(&hd, blk + 208, 2);
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        p[2 * (w >> 2) + (k & 1)] = fmaf((float)((q[w] >> (8 * k)) & 0xffu), x[4 * w + k], p[2 * (w >> 2) + (k & 1)]);
+    const float pa = fmaf(-32.0f, xs[0], p[0] + p[1]), pb = fmaf(-32.0f, xs[1], p[2] + p[3]);
+    return fmaf(half_bits(hd), fmaf(sa, pa, sb * pb), acc);
+  }
+  // The 32 weights of unit u, each rounded once: d scale is exact in fp32.
+  __device__ static inline void dequant(const uint8_t *blk, int u, float w[32]) {
+    uint32_t q[8];
+    codes(blk, u, q);
+    uint32_t hd = 0;
+    __builtin_memcpy(&hd, blk + 208, 2);
+    const float d = half_bits(hd);
+    const float da = d * (float)(int8_t)blk[192 + 2 * u], db = d * (float)(int8_t)blk[193 + 2 * u];
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[4 * v + k] = (v < 4 ? da : db) * (float)((int)((q[v] >> (8 * k)) & 0xffu) - 32);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -165,28 +278,42 @@ __device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f
 // as (p0 + p1) + (p2 + p3), the block scale applied once, blocks in c order.
 template <int FMT, int C>
 __device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane, int slice_n,
-                                             const float (&xr)[C][32]) {
+                                             const float (&xr)[C][32], const float (&xs)[C][2]) {
   using F = Fmt<FMT>;
   float s = 0.0f;
+  if constexpr (F::kUnits > 1) {
+    // K-quants: lane l's unit b = l + 64 c is sub-block b % 8 of the slice's
+    // super-block b / 8.
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int b = lane + 64 * c;
-    const int bo = ph + F::kBytes * b;  // block's byte offset in the staged row
-    // LDS reads at any byte alignment (gfx950 serves unaligned DS accesses):
-    // the payload needs no realignment in registers.
-    uint32_t sbits = 0, q[F::kWords];
-    __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
-    __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
-    float u[32];
-    F::decode(q, u);
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < C; ++c) {
+      const int b = lane + 64 * c;
+      const float acc = F::dot(sb + ph + F::kBytes * (b >> 3), b & 7, xr[c], xs[c], s);
+      s = b < slice_n ? acc : s;
+    }
+  } else {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
-    const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
-    s = b < slice_n ? blk_acc : s;
+    for (int c = 0; c < C; ++c) {
+      const int b = lane + 64 * c;
+      const int bo = ph + F::kBytes * b;  // block's byte offset in the staged row
+      // LDS reads at any byte alignment (gfx950 serves unaligned DS accesses):
+      // the payload needs no realignment in registers.
+      uint32_t sbits = 0, q[F::kWords];
+      __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
+      __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
+      float u[32];
+      F::decode(q, u);
+      float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
+      const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
+      s = b < slice_n ? blk_acc : s;
+    }
   }
   return s;
 }
+
+// The unit input sums row_partial takes for the 32-weight formats, which use none.
+template <int C> __device__ constexpr float kNoSums[C][2] = {};
 
 // Largest rows per chain tile, per (format, block columns per lane): a chain
 // wave holds its tile's fetched rows in registers until staged.
@@ -205,7 +332,7 @@ template <> struct TileCap<QG_MXFP4, 2> { static constexpr int value = 4; };
 // into their own place beyond the data, so every load is unconditional and
 // the number of loads per row is a constant the waits can count.
 template <int FMT, int C> struct Geo {
-  static constexpr int CH = (15 + 64 * C * Fmt<FMT>::kBytes + 15) / 16;  // granules a slice can touch
+  static constexpr int CH = (15 + 64 * C / Fmt<FMT>::kUnits * Fmt<FMT>::kBytes + 15) / 16;  // granules a slice can touch
   static constexpr int V = (CH + 63) / 64;                               // loads per lane per row
   static constexpr int SLOT = 1024 * V;                                  // ring slot bytes
 };
@@ -271,8 +398,9 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   const int64_t rb = a.row_bytes;
   const int slice_b0 = wave * SB;
   const int slice_n = max(0, min(SB, nb - slice_b0));  // >= 1 by the choice of WT
-  const int64_t slice_off = (int64_t)slice_b0 * Fmt<FMT>::kBytes;
-  const uint32_t slice_len = (uint32_t)slice_n * Fmt<FMT>::kBytes;
+  // (a wave's slice is whole blocks: 64 C units are 8 C K-quant super-blocks)
+  const int64_t slice_off = (int64_t)(slice_b0 / Fmt<FMT>::kUnits) * Fmt<FMT>::kBytes;
+  const uint32_t slice_len = (uint32_t)(slice_n / Fmt<FMT>::kUnits) * Fmt<FMT>::kBytes;
   const int T = gridDim.x;
   if ((int)blockIdx.x >= a.n_tiles) return;
 
@@ -345,6 +473,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   // wave_sum63, the runs in column order -- the team's waves cover every
   // column, so no extra read), then one scale per input.
   float xr[C][32];
+  float xs[C][2];  // K-quants: the sums of each unit's first and last 16 inputs
   constexpr int in_op = op_in(OP);
   auto load_x = [&](const float *x, const float *x2) {
 #pragma unroll
@@ -389,6 +518,23 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
 #pragma unroll
         for (int e = 0; e < 32; ++e) xr[c][e] *= inv;
       __syncthreads();  // ssq is read before a later window rewrites it
+    }
+    if constexpr (Fmt<FMT>::kUnits > 1) {
+      // Sums of the inputs as loaded: no multiply of a fused transform may
+      // be contracted into these adds, or a fused launch would not give the
+      // bits of the separate calls.
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          lo += xr[c][e];
+          hi += xr[c][16 + e];
+        }
+        xs[c][0] = lo;
+        xs[c][1] = hi;
+      }
     }
   };
 
@@ -452,7 +598,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
         wait_vmcnt<V * NB>();  // this row's copies have landed
         const uint8_t *sb = &ring[wave][slot][0];
         const int ph = (int)((ph0 + (uint32_t)i * rb16) & 15);
-        acc[i] = wave_sum63(row_partial<FMT, C>(sb, ph, lane, slice_n, xr));
+        acc[i] = wave_sum63(row_partial<FMT, C>(sb, ph, lane, slice_n, xr, xs));
         slot = slot + 1 == NS ? 0 : slot + 1;
       }
     }
@@ -509,6 +655,8 @@ GemvFn pick_op(int32_t fmt, Shape s) {
   switch (fmt) {
     case QG_Q8_0: return pick_fmt<QG_Q8_0, OP>(s);
     case QG_Q4_0: return pick_fmt<QG_Q4_0, OP>(s);
+    case QG_Q4_K: return pick_fmt<QG_Q4_K, OP>(s);
+    case QG_Q6_K: return pick_fmt<QG_Q6_K, OP>(s);
     default: return pick_fmt<QG_MXFP4, OP>(s);
   }
 }

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -40,7 +40,8 @@ def test_every_declared_symbol_is_exported():
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    assert re.search(r"QG_Q8_0 = 1, QG_Q4_0 = 2, QG_MXFP4 = 3", text)
+    assert re.search(rf"QG_Q8_0 = {q.Q8_0}, QG_Q4_0 = {q.Q4_0}, QG_MXFP4 = {q.MXFP4}, QG_Q4_K = {q.Q4_K}, "
+                     rf"QG_Q6_K = {q.Q6_K}", text)
     assert f"#define QG_MAX_WINDOWS {q.MAX_WINDOWS}" in text
     assert f"#define QG_MAX_K {q.MAX_K}" in text
     assert f"#define QG_CHAIN_MAX_K {q.CHAIN_MAX_K}" in text
@@ -61,8 +62,15 @@ def test_header_compiles_as_c():
 
 def test_sizes():
     L = q.lib()
-    assert [L.qgemv_block_bytes(f) for f in (1, 2, 3)] == [34, 18, 17]
-    assert L.qgemv_block_bytes(0) == E_FMT and L.qgemv_block_bytes(4) == E_FMT
+    assert [L.qgemv_block_bytes(f) for f in (1, 2, 3, 4, 5)] == [34, 18, 17, 144, 210]
+    assert [L.qgemv_block_weights(f) for f in (1, 2, 3, 4, 5)] == [32, 32, 32, 256, 256]
+    assert L.qgemv_block_bytes(0) == E_FMT and L.qgemv_block_bytes(6) == E_FMT
+    assert L.qgemv_block_weights(0) == E_FMT and L.qgemv_block_weights(6) == E_FMT
+    # K-quants: k a multiple of 256; 6144 x 6144 Q4_K is 4.5 bits per weight
+    assert L.qgemv_weight_bytes(4, 6144, 6144) == 6144 * 6144 * 9 // 16
+    assert L.qgemv_weight_bytes(5, 2, 512) == 2 * 2 * 210
+    assert L.qgemv_weight_bytes(4, 4, 288) == E_SHAPE
+    assert L.qgemv_weight_bytes(5, 4, 32) == E_SHAPE
     assert L.qgemv_weight_bytes(3, 2880, 2880) == 4_406_400
     assert L.qgemv_weight_bytes(2, 4096, 4096) == 9_437_184
     assert L.qgemv_weight_bytes(1, 11008, 4096) == 47_906_816
@@ -77,7 +85,8 @@ FAKE = 0x1000  # a non-NULL address; never dereferenced by a call that fails val
 
 
 def mat(fmt=1, rows=8, k=64, nbytes=None, data=FAKE, reserved=0):
-    n = rows * (k // 32) * {1: 34, 2: 18, 3: 17}.get(fmt, 34) if nbytes is None else nbytes
+    n = rows * (k // 32) * {1: 34, 2: 18, 3: 17, 4: 18, 5: 26.25}.get(fmt, 34) if nbytes is None else nbytes
+    n = int(n)
     return qg_matrix(data, fmt, reserved, rows, k, n)
 
 
@@ -87,8 +96,15 @@ def rows_call(m, r0=0, r1=8, x=FAKE, y=FAKE, B=0):
 
 def test_qgemv_rows_validation():
     assert rows_call(None) == E_NULL
-    assert rows_call(mat(fmt=5)) == E_FMT
+    assert rows_call(mat(fmt=6)) == E_FMT
+    assert rows_call(mat(fmt=0)) == E_FMT
     assert rows_call(mat(k=48, nbytes=0)) == E_SHAPE
+    # K-quants: k a multiple of 256, n_bytes whole super-blocks
+    assert rows_call(mat(fmt=4, k=288, nbytes=0)) == E_SHAPE
+    assert rows_call(mat(fmt=5, k=32, nbytes=0)) == E_SHAPE
+    assert rows_call(mat(fmt=4, k=512, nbytes=8 * 2 * 144 - 1)) == E_SIZE
+    assert rows_call(mat(fmt=5, k=512, nbytes=8 * 2 * 210 + 16)) == E_SIZE
+    assert rows_call(mat(fmt=5, k=512, nbytes=8 * 2 * 210), r1=9) == E_RANGE
     assert rows_call(mat(k=49152 + 32)) == E_SHAPE
     assert rows_call(mat(data=FAKE + 8)) == E_ARG  # not 16-byte aligned
     assert rows_call(mat(nbytes=8 * 2 * 34 - 1)) == E_SIZE
@@ -192,7 +208,7 @@ def test_rows_op_validation():
         return L.qgemv_rows_op(ctypes.byref(m), r0, r1, x, x2, in_op, eps, out_op, y, B, None)
 
     assert L.qgemv_rows_op(None, 0, 8, FAKE, FAKE, 0, 0.0, 0, FAKE, 0, None) == E_NULL
-    assert call(m=mat(fmt=5)) == E_FMT
+    assert call(m=mat(fmt=6)) == E_FMT
     assert call(r1=9) == E_RANGE
     assert call(B=-1) == E_ARG
     assert call(in_op=2) == E_ARG  # GELU_RMS: GELU belongs to the producer (QG_OUT_GELU)
@@ -216,7 +232,7 @@ def test_mapped_validation():
         return L.qgemv_mapped_rows(ctypes.byref(m) if m is not None else None, r0, r1, x, y, B, None)
 
     assert call(None) == E_NULL
-    assert call(mat(fmt=5)) == E_FMT
+    assert call(mat(fmt=6)) == E_FMT
     assert call(mat(k=48, nbytes=0)) == E_SHAPE
     assert call(mat(data=FAKE + 4)) == E_ARG
     assert call(mat(nbytes=8 * 2 * 34 - 1)) == E_SIZE
@@ -272,7 +288,8 @@ def test_chain_validation():
     ok_w = [cwin(), cwin(2, 5)]
     assert create([cstep(n=2)], ok_w, out=False) == E_NULL
     assert L.qgemv_chain_create(1, None, 1, (q.qg_chain_window * 1)(cwin()), 1, ctypes.byref(h)) == E_NULL
-    assert create([cstep()], ok_w, fmt=4) == E_FMT
+    for f in (0, 4, 5, 6):  # the K-quants have no chain kernel
+        assert create([cstep()], ok_w, fmt=f) == E_FMT
     assert create([], ok_w) == E_ARG
     assert create([cstep()], []) == E_ARG
     assert create([cstep(k=48)], ok_w) == E_SHAPE

@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(q.Q8_0, 300, 6144), (q.Q8_0, 97, 24576), (q.Q4_0, 257, 4096), (q.MXFP4, 200, 2880),
           (q.Q8_0, 65, 32), (q.Q4_0, 40, 2080), (q.Q8_0, 33, 32768)]
+KSHAPES = [(q.Q4_K, 130, 6144), (q.Q6_K, 71, 24576), (q.Q4_K, 40, 256)]
 
 
 def dput(a, dev):
@@ -36,7 +37,7 @@ def setup(dev, fmt, rows, k, tag):
     return w, x, x2, q.Matrix(dput(w, dev), fmt, rows, k)
 
 
-@pytest.mark.parametrize("fmt,rows,k", SHAPES)
+@pytest.mark.parametrize("fmt,rows,k", SHAPES + KSHAPES)
 def test_fused_rms_equals_separate(dev, fmt, rows, k):
     import torch
     w, x, _, M = setup(dev, fmt, rows, k, 1)
@@ -55,7 +56,7 @@ def test_fused_rms_equals_separate(dev, fmt, rows, k):
     check(ref.cpu().numpy(), r, a, what="fused rms vs oracle")
 
 
-@pytest.mark.parametrize("fmt,rows,k", SHAPES[:4])
+@pytest.mark.parametrize("fmt,rows,k", SHAPES[:4] + KSHAPES)
 def test_fused_silu_mul_equals_separate(dev, fmt, rows, k):
     import torch
     w, x, x2, M = setup(dev, fmt, rows, k, 2)
@@ -70,14 +71,15 @@ def test_fused_silu_mul_equals_separate(dev, fmt, rows, k):
     assert bits_equal(y.cpu().numpy(), ref.cpu().numpy())
 
 
-@pytest.mark.parametrize("fmt,rows,k", SHAPES[:4])
+@pytest.mark.parametrize("fmt,rows,k", SHAPES[:4] + KSHAPES)
 def test_fused_gelu_then_rms_equals_separate(dev, fmt, rows, k):
     """producer stores gelu(y) (QG_OUT_GELU), consumer normalises it
     (QG_IN_RMS): equal to qgemv_rows, qgemv_rms_carry(gelu=1), qgemv_rows."""
     import torch
     w, x, _, M = setup(dev, fmt, rows, k, 3)
-    w2 = synth.blocks(fmt, 64, 32 * ((rows + 31) // 32), synth.seed_of(8, 70 + fmt))
-    kk = 32 * ((rows + 31) // 32)
+    qk = synth.BLOCK_WEIGHTS[fmt]
+    kk = qk * ((rows + qk - 1) // qk)
+    w2 = synth.blocks(fmt, 64, kk, synth.seed_of(8, 70 + fmt))
     M2 = q.Matrix(dput(w2, dev), fmt, 64, kk)
     xd = dput(x, dev)
     f32 = dict(dtype=torch.float32, device=dev)

@@ -34,7 +34,8 @@ def sync():
 
 
 @pytest.mark.parametrize("fmt,rows,k", [(q.Q8_0, 11008, 4096), (q.Q4_0, 4096, 4096), (q.MXFP4, 2880, 2880),
-                                        (q.Q8_0, 77, 24576), (q.Q4_0, 33, 96)])
+                                        (q.Q8_0, 77, 24576), (q.Q4_0, 33, 96), (q.Q4_K, 1000, 4096),
+                                        (q.Q6_K, 300, 11008)])
 def test_mapped_rows_equal_resident(dev, fmt, rows, k):
     import torch
     w = synth.blocks(fmt, rows, k, synth.seed_of(7, fmt))
