@@ -17,7 +17,9 @@ dominant kernel (its launches timed with HIP events on the launch stream), the
 CPU oracle timed on a bounded sample of the same pass, and a sampled parity
 check of the GPU results against the oracle.
 
-Other workloads (--workload): q4_0_4096, moe_mxfp4, ffn_streamed, q8_0_256.
+Other workloads (--workload): q4_0_4096, moe_mxfp4, ffn_streamed, q8_0_256, and
+q4_k_m_dense20b (the same pass with Q4_K QKV/out/up and a Q6_K down
+projection, 12.9 GB).
 """
 from __future__ import annotations
 
@@ -93,24 +95,27 @@ def cpu_model() -> str:
 class DensePass:
     """Weights, buffers and prepared C-ABI calls of the synthetic dense model."""
 
-    def __init__(self, layers, hidden, ffn, dev, eps=1e-6, verbose=True):
+    def __init__(self, layers, hidden, ffn, dev, eps=1e-6, verbose=True, cfg=5):
         import torch
         import quantized_gemv_gguf_amd as q
         self.q, self.torch = q, torch
         self.L, self.H, self.F, self.dev, self.eps = layers, hidden, ffn, dev, eps
+        self.cfg = cfg
+        self.fmts = synth.CONFIGS[cfg]["fmts"]  # format of qkv, out, up, down
         self.shapes = synth.dense_layer_shapes(hidden, ffn)
         self.lib = q.lib()
         self.stream = torch.cuda.current_stream().cuda_stream
         t0 = time.time()
-        maxbytes = max(r * (k // 32) * 34 for _, r, k in self.shapes)
+        maxbytes = max(r * synth.row_bytes(f, k) for f, (_, r, k) in zip(self.fmts, self.shapes))
         staging = torch.empty(maxbytes, dtype=torch.uint8, pin_memory=True)
         self.w = []  # [layer][matrix] device tensors
         for l in range(layers):
             row = []
             for m, (_, r, k) in enumerate(self.shapes):
-                nbytes = r * (k // 32) * 34
-                view = staging[:nbytes].numpy().reshape(r, (k // 32) * 34)
-                synth.blocks(synth.Q8_0, r, k, self.seed(l, m), out=view, threads=threads())
+                f = self.fmts[m]
+                nbytes = r * synth.row_bytes(f, k)
+                view = staging[:nbytes].numpy().reshape(r, synth.row_bytes(f, k))
+                synth.blocks(f, r, k, self.seed(l, m), out=view, threads=threads())
                 t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
                 t.copy_(staging[:nbytes], non_blocking=False)
                 row.append(t)
@@ -132,7 +137,7 @@ class DensePass:
         self.mats, self.calls = [], []
         for l in range(layers):
             for m, (_, r, k) in enumerate(self.shapes):
-                cm = q.qg_matrix(self.w[l][m].data_ptr(), q.Q8_0, 0, r, k, self.w[l][m].numel())
+                cm = q.qg_matrix(self.w[l][m].data_ptr(), self.fmts[m], 0, r, k, self.w[l][m].numel())
                 self.mats.append(cm)
                 self.calls.append((ctypes.byref(cm), r, ins[m].data_ptr(), outs[m].data_ptr(),
                                    self.w[l][m].numel(), k, m))
@@ -149,9 +154,12 @@ class DensePass:
                 self.fcalls.append((mp, r, fin[m], fout[m].data_ptr(), nbytes, k, m,
                                     q.OUT_GELU if m == 2 else q.OUT_Y))
 
-    @staticmethod
-    def seed(layer, m):
-        return synth.seed_of(5, 4 * layer + m)
+    def seed(self, layer, m):
+        return synth.seed_of(self.cfg, 4 * layer + m)
+
+    def kernel_name(self, m):
+        """Name of the GEMV variant matrix m of a layer runs: format and k."""
+        return f"gemv_{synth.FMT_NAMES[self.fmts[m]]}_k{self.shapes[m][2]}"
 
     # -- the pass as one chain: one persistent launch per token --
     def build_chain(self):
@@ -160,6 +168,8 @@ class DensePass:
         `xin`, which the first step of the next token normalises."""
         torch, q = self.torch, self.q
         H, F = self.H, self.F
+        if set(self.fmts) != {q.Q8_0}:
+            raise ValueError("chains run the 32-weight formats only")
         f32 = dict(dtype=torch.float32, device=self.dev)
         self.xin = self.x0.clone()
         self.ys = []
@@ -240,11 +250,14 @@ class DensePass:
                 raise RuntimeError(f"qgemv_rms_carry failed: {rc}")
 
 
-def dense_workload(args, dev):
+FMT_LABEL = {5: "Q8_0", 6: "Q4_K (QKV, out, up) + Q6_K (down)"}
+
+
+def dense_workload(args, dev, cfg=5):
     import torch
-    c = synth.CONFIGS[5]
+    c = synth.CONFIGS[cfg]
     layers = args.layers or c["layers"]
-    model = DensePass(layers, c["hidden"], c["ffn"], dev)
+    model = DensePass(layers, c["hidden"], c["ffn"], dev, cfg=cfg)
     if args.chain:
         return dense_chain_workload(args, dev, model, c, layers)
     torch.cuda.synchronize()
@@ -287,8 +300,8 @@ def dense_workload(args, dev):
     # one pair of HIP events (an event pair around every single launch would
     # add its own packets and gaps to each measured launch)
     per_k = {}
-    for kk in sorted({c_[5] for c_ in model.fcalls}):
-        sub = [i for i, c_ in enumerate(model.fcalls) if c_[5] == kk]
+    for kk in sorted({model.kernel_name(c_[6]) for c_ in model.fcalls}):
+        sub = [i for i, c_ in enumerate(model.fcalls) if model.kernel_name(c_[6]) == kk]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(2):
@@ -300,8 +313,8 @@ def dense_workload(args, dev):
     gbs = total_bytes / wall / 1e9
     kernels = {}
     for k, (b, ms, cnt) in sorted(per_k.items()):
-        kernels[f"gemv_q8_0_k{k}"] = {"launches": cnt, "avg_us": ms / cnt * 1e3, "avg_bytes": b / cnt,
-                                      "GBs": b / (ms / 1e3) / 1e9}
+        kernels[k] = {"launches": cnt, "avg_us": ms / cnt * 1e3, "avg_bytes": b / cnt,
+                      "GBs": b / (ms / 1e3) / 1e9}
     dom_k = max(per_k, key=lambda k: per_k[k][1])
     b, ms, cnt = per_k[dom_k]
     achieved = b / (ms / 1e3) / 1e9
@@ -313,13 +326,13 @@ def dense_workload(args, dev):
         "gpu_event_ms_per_step": gpu_ms / args.steps,
         "bytes_per_token": model.bytes_per_token,
         "config": {"workload": c["name"], "layers": layers, "hidden": c["hidden"], "ffn": c["ffn"],
-                   "format": "Q8_0", "tokens": args.steps, "gemvs_per_token": n,
+                   "format": FMT_LABEL[cfg], "tokens": args.steps, "gemvs_per_token": n,
                    "weight_bytes_per_token": model.bytes_per_token,
                    "launch": "176 fused GEMV launches per token (RMS carry in the x-load, GELU in the store)"
                              + (", one HIP graph per token" if graph is not None else "")},
-        "roofline": {"bound": "hbm", "kernel": f"gemv_q8_0_k{dom_k}", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": dom_k, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic(f"gemv_q8_0_k{dom_k}"), "avg_launch_us": ms / cnt * 1e3,
+                     "traffic": profiled_traffic(dom_k), "avg_launch_us": ms / cnt * 1e3,
                      "bytes_per_launch": b / cnt},
         "kernels": kernels,
     }
@@ -457,8 +470,9 @@ def dense_parity(model, layers, n_rows=48, seed=7):
         rows = np.sort(rng.choice(r, n_rows, replace=False))
         ref, a = np.empty(n_rows), np.empty(n_rows)
         for j, row in enumerate(rows):
-            wrow = synth.blocks(synth.Q8_0, r, k, model.seed(i // 4, m), r0=int(row), r1=int(row) + 1, threads=1)
-            ref[j], a[j] = [v[0] for v in oracle.gemv_rows(oracle.Q8_0, wrow, 1, k, x, threads=1)]
+            f = model.fmts[m]
+            wrow = synth.blocks(f, r, k, model.seed(i // 4, m), r0=int(row), r1=int(row) + 1, threads=1)
+            ref[j], a[j] = [v[0] for v in oracle.gemv_rows(f, wrow, 1, k, x, threads=1)]
         if m == 2:  # the stored output is gelu(u): compare u's GELU in fp64
             from math import erfc, sqrt
             ref = np.array([0.5 * v * erfc(-v / sqrt(2.0)) for v in ref])
@@ -466,8 +480,12 @@ def dense_parity(model, layers, n_rows=48, seed=7):
             # rounding error relative to |gelu(u)|
             a = 1.13 * a + np.abs(ref)
         err = np.abs(y[rows] - ref)
-        worst_c = max(worst_c, float(np.max(err / a)))
-        worst_n = max(worst_n, float(err.max() / np.abs(ref).max()))
+        with np.errstate(invalid="ignore", divide="ignore"):
+            c_ = float(np.max(err / a))
+            n_ = float(err.max() / np.abs(ref).max())
+        # a degenerate sample (all-zero or non-finite rows) fails the check
+        worst_c = max(worst_c, c_ if np.isfinite(c_) else np.inf)
+        worst_n = max(worst_n, n_ if np.isfinite(n_) else np.inf)
         checked += n_rows
 
     torch.cuda.synchronize()
@@ -492,16 +510,17 @@ def dense_cpu_baseline(model, seconds):
     tok = 0
     while t_oracle < seconds:
         for l in range(model.L):
-            ws = [synth.blocks(synth.Q8_0, r, k, model.seed(l, m), threads=nth)
+            fm = model.fmts
+            ws = [synth.blocks(fm[m], r, k, model.seed(l, m), threads=nth)
                   for m, (_, r, k) in enumerate(model.shapes)]
             t = time.perf_counter()
-            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
+            y, _ = oracle.gemv_rows(fm[0], ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
             c = oracle.rms_carry(y[2 * model.H:3 * model.H], model.eps)
-            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[1], *model.shapes[1][1:], c.astype(np.float32), threads=nth)
+            y, _ = oracle.gemv_rows(fm[1], ws[1], *model.shapes[1][1:], c.astype(np.float32), threads=nth)
             c = oracle.rms_carry(y, model.eps)
-            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[2], *model.shapes[2][1:], c.astype(np.float32), threads=nth)
+            y, _ = oracle.gemv_rows(fm[2], ws[2], *model.shapes[2][1:], c.astype(np.float32), threads=nth)
             act = oracle.rms_carry(y, model.eps, gelu=True)
-            y, _ = oracle.gemv_rows(oracle.Q8_0, ws[3], *model.shapes[3][1:], act.astype(np.float32), threads=nth)
+            y, _ = oracle.gemv_rows(fm[3], ws[3], *model.shapes[3][1:], act.astype(np.float32), threads=nth)
             c = oracle.rms_carry(y, model.eps)
             t_oracle += time.perf_counter() - t
             nbytes += sum(w.nbytes for w in ws)
@@ -512,8 +531,9 @@ def dense_cpu_baseline(model, seconds):
     gbs = nbytes / t_oracle / 1e9
     return {"value": gbs, "unit": "GB/s", "cores": nth, "kind": "oracle",
             "tokens_per_s_equiv": gbs * 1e9 / model.bytes_per_token,
-            "sample": f"{layers_done} layer passes ({4 * layers_done} GEMVs, {nbytes / 1e9:.2f} GB of Q8_0 "
-                      f"weights, {tok} token(s) of the same 44-layer pass), fp64 scalar C oracle, "
+            "sample": f"{layers_done} layer passes ({4 * layers_done} GEMVs, {nbytes / 1e9:.2f} GB of "
+                      f"{FMT_LABEL[model.cfg]} weights, {tok} token(s) of the same {model.L}-layer pass), "
+                      f"fp64 scalar C oracle, "
                       f"{nth} threads, {t_oracle:.1f} s",
             "cpu": cpu_model()}
 
@@ -752,8 +772,14 @@ def q8_0_small_workload(args, dev):
             "config": {"workload": c["name"], "format": "Q8_0", "rows": rows, "k": k,
                        "note": "weights stay in cache across launches; a latency figure, not an HBM one"}}
 
+def kquant_dense_workload(args, dev):
+    """The dense 20B-class pass in the Q4_K_M mix: Q4_K QKV, out and up, Q6_K down."""
+    return dense_workload(args, dev, cfg=6)
+
+
 WORKLOADS = {"dense20b": dense_workload, "q4_0_4096": q4_0_workload, "moe_mxfp4": moe_workload,
-             "ffn_streamed": ffn_streamed_workload, "q8_0_256": q8_0_small_workload}
+             "ffn_streamed": ffn_streamed_workload, "q8_0_256": q8_0_small_workload,
+             "q4_k_m_dense20b": kquant_dense_workload}
 
 
 # --- entry --------------------------------------------------------------------------

@@ -114,6 +114,11 @@ template <> struct Fmt<QG_MXFP4> {
 };
 
 __device__ __forceinline__ float half_bits(uint32_t h) { return __half2float(__ushort_as_half((uint16_t)h)); }
+// The fp16 in the low / high half of a word, widened (exact, subnormals kept).
+__device__ __forceinline__ float h16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); }
+__device__ __forceinline__ float h16_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
 
 // Q4_K: 144-byte super-block of 256 weights = fp16 d, fp16 dmin, 12 bytes of
 // packed 6-bit sub-block scales sc and mins m, 128 bytes of nibbles;
@@ -123,7 +128,11 @@ __device__ __forceinline__ float half_bits(uint32_t h) { return __half2float(__u
 // bits in the top bits of bytes s - 4 (sc) and s (m).  The codes of
 // sub-block s are one nibble (low for even s) of bytes 32 (s / 2) .. + 31.
 // A unit's dot is d sc (sum q x) - dmin m (sum x), with sum x formed once per
-// activation vector.
+// activation vector.  The GEMV takes two codes per 32-bit word as fp16
+// subnormals, q 2^-24 (or 16 q 2^-24 for an odd sub-block's high nibbles,
+// masked in place), which v_fma_mix_f32 multiplies into the fp32 sums with
+// no separate conversion; the power of two comes back in the scale, so the
+// sums are those of the plain codes, bit for bit.
 template <> struct Fmt<QG_Q4_K> {
   static constexpr int kBytes = 144, kUnits = 8;
   __device__ static inline void scale_min(const uint8_t *blk, int s, int &sc, int &m) {
@@ -131,12 +140,14 @@ template <> struct Fmt<QG_Q4_K> {
     sc = s < 4 ? (a & 63) : ((c & 15) | ((a >> 6) << 4));
     m = s < 4 ? (b & 63) : ((c >> 4) | ((b >> 6) << 4));
   }
+  // The sub-block's codes, scaled by 16 for odd s, and that scale's inverse.
   template <typename P>
-  __device__ static inline void codes(const P *blk, int s, uint32_t q[8]) {
+  __device__ static inline float codes(const P *blk, int s, uint32_t q[8]) {
     __builtin_memcpy(q, blk + 16 + 32 * (s >> 1), 32);
-    const int sh = 4 * (s & 1);
+    const uint32_t mask = (s & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = (q[i] >> sh) & 0x0F0F0F0Fu;
+    for (int i = 0; i < 8; ++i) q[i] &= mask;
+    return (s & 1) ? 0.0625f : 1.0f;
   }
   __device__ static inline float dot(const uint8_t *blk, int s, const float (&x)[32], const float (&xs)[2],
                                      float acc) {
@@ -145,25 +156,32 @@ template <> struct Fmt<QG_Q4_K> {
     int sc, m;
     scale_min(blk, s, sc, m);
     uint32_t q[8];
-    codes(blk, s, q);
+    __builtin_memcpy(q, blk + 16 + 32 * (s >> 1), 32);
+    // codes of bytes 0 and 2 (then 1 and 3) of a word as two fp16 subnormals
+    const uint32_t mask = (s & 1) ? 0x00F000F0u : 0x000F000Fu;
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) p[k] = fmaf((float)((q[i] >> (8 * k)) & 0xffu), x[4 * i + k], p[k]);
-    acc = fmaf(half_bits(hd) * (float)sc, (p[0] + p[1]) + (p[2] + p[3]), acc);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = q[i] & mask, b = (q[i] >> 8) & mask;
+      p[0] = fmaf(h16_lo(a), x[4 * i + 0], p[0]);
+      p[1] = fmaf(h16_lo(b), x[4 * i + 1], p[1]);
+      p[2] = fmaf(h16_hi(a), x[4 * i + 2], p[2]);
+      p[3] = fmaf(h16_hi(b), x[4 * i + 3], p[3]);
+    }
+    const float f = (s & 1) ? 0x1p20f : 0x1p24f;
+    acc = fmaf(half_bits(hd) * (float)sc * f, (p[0] + p[1]) + (p[2] + p[3]), acc);
     return fmaf(-(half_bits(hd >> 16) * (float)m), xs[0] + xs[1], acc);
   }
   // The 32 weights of sub-block s, each rounded once: d sc q and dmin m are
-  // exact in fp32.
+  // exact in fp32 (so is d sc / 16 times 16 q).
   __device__ static inline void dequant(const uint8_t *blk, int s, float w[32]) {
     uint32_t hd;
     __builtin_memcpy(&hd, blk, 4);
     int sc, m;
     scale_min(blk, s, sc, m);
     uint32_t q[8];
-    codes(blk, s, q);
-    const float ds = half_bits(hd) * (float)sc, mm = half_bits(hd >> 16) * (float)m;
+    const float f = codes(blk, s, q);
+    const float ds = half_bits(hd) * (float)sc * f, mm = half_bits(hd >> 16) * (float)m;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -187,9 +205,12 @@ template <> struct Fmt<QG_Q6_K> {
     uint32_t lo[8], hi[8];
     __builtin_memcpy(lo, blk + 64 * h + 32 * (i & 1), 32);
     __builtin_memcpy(hi, blk + 128 + 32 * h, 32);
-    const int s4 = 4 * (i >> 1), s2 = 2 * i;
+    // bits 2 i, 2 i + 1 of each high byte move to bits 4, 5 by one rotation
+    // (bits that wrap into another byte land outside the kept field)
+    const int s4 = 4 * (i >> 1), rot = (2 * i - 4) & 31;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) q[w] = ((lo[w] >> s4) & 0x0F0F0F0Fu) | (((hi[w] >> s2) & 0x03030303u) << 4);
+    for (int w = 0; w < 8; ++w)
+      q[w] = ((lo[w] >> s4) & 0x0F0F0F0Fu) | (__builtin_amdgcn_alignbit(hi[w], hi[w], rot) & 0x30303030u);
   }
   __device__ static inline float dot(const uint8_t *blk, int u, const float (&x)[32], const float (&xs)[2],
                                      float acc) {

@@ -91,7 +91,8 @@ def blocks(fmt: int, n_rows: int, k: int, seed: int, r0: int = 0, r1: int | None
       Q8_0 : d ~ fp16(U[1e-3, 1e-2)) * (+-1), q ~ U{-127..127}
       Q4_0 : d ~ fp16(U[1e-3, 1e-2)), every code byte ~ U{0..255}
       MXFP4: e ~ U{118..130}, every code byte ~ U{0..255}
-      Q4_K : d, dmin ~ fp16(U[1e-4, 1e-3)), scale/min and code bytes ~ U{0..255}
+      Q4_K : d ~ fp16(U[1e-4, 1e-3)), dmin = 8 d, sub-block scales sc ~ U{0..63},
+             mins m = round(15 sc / 16) (centred sub-blocks), code bytes ~ U{0..255}
       Q6_K : d ~ fp16(U[1e-4, 1e-3)), code bytes ~ U{0..255}, scales ~ U{-127..127}
     ``out`` (optional) is a C-contiguous uint8 array of the result's shape.
     """
@@ -145,7 +146,7 @@ def expert_ids(n_expert: int, n_sel: int, n_tokens: int, seed: int) -> np.ndarra
     return ids.astype(np.int32)
 
 
-# --- the five workloads --------------------------------------------------------
+# --- the workloads ----------------------------------------------------------------
 
 def seed_of(cfg: int, tensor_id: int) -> int:
     return 1000 * cfg + tensor_id
@@ -159,7 +160,11 @@ CONFIGS = {
     4: dict(name="mxfp4_moe_128x2880x2880_top4", fmt=MXFP4, n_expert=128, out=2880, k=2880,
             n_sel=4, tokens=64, block_rows=(0, 128, 512)),
     5: dict(name="q8_0_dense20b_44L_h6144_f24576", fmt=Q8_0, layers=44, hidden=6144, ffn=24576,
-            tokens=32),
+            tokens=32, fmts=(Q8_0, Q8_0, Q8_0, Q8_0)),
+    # the same pass in the K-quant mix of a "Q4_K_M" file: Q4_K with a Q6_K
+    # down projection (12.9 GB resident)
+    6: dict(name="q4_k_m_dense20b_44L_h6144_f24576", fmt=Q4_K, layers=44, hidden=6144, ffn=24576,
+            tokens=32, fmts=(Q4_K, Q4_K, Q4_K, Q6_K)),
 }
 
 

@@ -19,8 +19,14 @@
  *   Q4_0 : d as above; 16 code bytes uniform over 0..255.
  *   MXFP4: scale byte uniform over {e_lo..e_hi}; 16 code bytes uniform.
  * and per 256-weight super-block:
- *   Q4_K : d and dmin each as d above (dmin from its own stream, no sign);
- *          the 12 scale/min bytes and 128 code bytes uniform over 0..255.
+ *   Q4_K : d as above, dmin = 8 d (exact: three more in the fp16 exponent);
+ *          eight 6-bit sub-block scales sc uniform over 0..63, each min
+ *          m = round(15 sc / 16), so that every sub-block's weights centre on
+ *          zero as a quantiser's blocks do (d sc q - 8 d m ~ d sc (q - 7.5));
+ *          the 16 fields packed into 12 bytes in GGUF's layout (fields 0..3
+ *          in the low six bits of bytes 0..3 / 4..7, fields 4..7 as nibbles of
+ *          bytes 8..11 with their top two bits in the top bits of bytes
+ *          0..3 / 4..7); 128 code bytes uniform over 0..255.
  *   Q6_K : d as above (stored last); 192 low/high code bytes uniform over
  *          0..255; 16 int8 scales uniform over {-127..127}.
  */
@@ -77,14 +83,25 @@ static void put_half(uint8_t *p, uint16_t h) {
 }
 
 static void fill_block(const job_t *j, uint64_t b, uint8_t *p) {
-  /* stream 0: scale, stream 1: codes, stream 3: Q4_K's dmin, stream 4: Q6_K's scales */
+  /* stream 0: scale, stream 1: codes, stream 3: Q4_K's sub-block scales, stream 4: Q6_K's scales */
   if (j->fmt == SY_Q4_K) {
-    put_half(p, draw_half(j, 0, b));
-    put_half(p + 2, draw_half(j, 3, b));
-    for (int i = 0; i < 18; ++i) {  /* 140 bytes from 18 words */
-      uint64_t w = sm64(j->seed, 1, 18 * b + i);
-      int n = i < 17 ? 8 : 4;
-      memcpy(p + 4 + 8 * i, &w, (size_t)n);
+    uint16_t d = draw_half(j, 0, b);
+    put_half(p, d);
+    put_half(p + 2, (uint16_t)(d + (3 << 10)));
+    uint64_t r = sm64(j->seed, 3, b);
+    int sc[8], m[8];
+    for (int f = 0; f < 8; ++f) {
+      sc[f] = (int)((r >> (6 * f)) & 63);
+      m[f] = (15 * sc[f] + 8) >> 4;
+    }
+    for (int f = 0; f < 4; ++f) {
+      p[4 + f] = (uint8_t)((sc[f] & 63) | ((sc[f + 4] >> 4) << 6));
+      p[8 + f] = (uint8_t)((m[f] & 63) | ((m[f + 4] >> 4) << 6));
+      p[12 + f] = (uint8_t)((sc[f + 4] & 15) | ((m[f + 4] & 15) << 4));
+    }
+    for (int i = 0; i < 16; ++i) {  /* 128 code bytes */
+      uint64_t w = sm64(j->seed, 1, 16 * b + i);
+      memcpy(p + 16 + 8 * i, &w, 8);
     }
     return;
   }
