@@ -19,7 +19,8 @@ check of the GPU results against the oracle.
 
 Other workloads (--workload): q4_0_4096, moe_mxfp4, ffn_streamed, q8_0_256, and
 q4_k_m_dense20b (the same pass with Q4_K QKV/out/up and a Q6_K down
-projection, 12.9 GB).
+projection, 12.9 GB), dense20b_batch (--batch tokens per step through
+qgemv_rows_batch).
 """
 from __future__ import annotations
 
@@ -772,6 +773,74 @@ def q8_0_small_workload(args, dev):
             "config": {"workload": c["name"], "format": "Q8_0", "rows": rows, "k": k,
                        "note": "weights stay in cache across launches; a latency figure, not an HBM one"}}
 
+def dense_batch_workload(args, dev):
+    """The dense 20B-class pass (Q8_0, or --kquant for the Q4_K_M mix) with
+    --batch tokens per step: every GEMV a qgemv_rows_batch call on that many
+    fixed activation vectors (no carries between GEMVs: a batch of decode
+    streams each has its own).  Reported: tokens/s and the weight bytes the
+    passes read per step (a pass reads the matrix once for up to four tokens)."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    import oracle
+    cfg = 6 if args.kquant else 5
+    c = synth.CONFIGS[cfg]
+    layers = args.layers or c["layers"]
+    B = args.batch
+    model = DensePass(layers, c["hidden"], c["ffn"], dev, cfg=cfg)
+    H, F = c["hidden"], c["ffn"]
+    X = {k: torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(10, 1000 * (k // 1024) + t))
+                                        for t in range(B)])).to(dev) for k in (H, F)}
+    Y = [torch.empty((B, r), dtype=torch.float32, device=dev) for _, r, _ in model.shapes]
+    L, st = model.lib, model.stream
+
+    def passes(k):
+        """Tokens per pass for this k (the library's choice, restated for the byte count)."""
+        nb = k // 32
+        wt1 = -(-nb // 64)
+        c_ = 1 if (wt1 <= 12 and model.fmts[0] != q.Q4_0) else 2
+        out, left = [], B
+        while left > 0:
+            wt = -(-nb // (64 * c_))
+            nt = 4 if left >= 4 and c_ == 1 and wt <= 8 else 2 if left >= 2 and (c_ == 1 or wt <= 8) else 1
+            out.append(nt)
+            left -= nt
+        return out
+
+    def step(_=0):
+        for i, (mp, r, _, _, nbytes, k, m) in enumerate(model.calls):
+            rc = L.qgemv_rows_batch(mp, 0, r, X[k].data_ptr(), k, B, Y[m].data_ptr(), r, 0, st)
+            if rc != 0:
+                raise RuntimeError(f"qgemv_rows_batch failed: {rc}")
+
+    for _ in range(args.warmup):
+        step()
+    wall, gpu_ms = _timed(step, args.steps, torch)
+    per_step_read = sum(len(passes(k)) * nbytes for (_, r, _, _, nbytes, k, m) in model.calls)
+    tok_bytes = model.bytes_per_token * B
+    # parity: sampled rows of the first layer's four GEMVs, every token
+    worst = 0.0
+    rng = np.random.default_rng(3)
+    step()
+    torch.cuda.synchronize()
+    for m, (_, r, k) in enumerate(model.shapes):
+        y = Y[m].cpu().numpy()  # the last layer's outputs
+        rows = np.sort(rng.choice(r, 16, replace=False))
+        for row in rows:
+            wrow = synth.blocks(model.fmts[m], r, k, model.seed(layers - 1, m), r0=int(row), r1=int(row) + 1,
+                                threads=1)
+            for t in range(B):
+                ref, a = oracle.gemv_rows(model.fmts[m], wrow, 1, k, X[k][t].cpu().numpy(), threads=1)
+                worst = max(worst, float(abs(y[t, row] - ref[0]) / a[0]) if a[0] > 0 else np.inf)
+    return {"value": per_step_read * args.steps / wall / 1e9, "ms_per_step": wall / args.steps * 1e3,
+            "tokens_per_s": B * args.steps / wall, "token_equiv_GBs": tok_bytes * args.steps / wall / 1e9,
+            "bytes_read_per_step": per_step_read, "weight_bytes_per_token": model.bytes_per_token,
+            "config": {"workload": c["name"] + f"_batch{B}", "layers": layers, "format": FMT_LABEL[cfg],
+                       "tokens_per_step": B, "passes_per_gemv": {str(k): passes(k) for k in (H, F)},
+                       "launch": "176 qgemv_rows_batch calls per step"},
+            "parity": {"rows_checked": 16 * 4 * B, "max_componentwise": worst, "tol": TOL,
+                       "pass": bool(worst <= TOL)}}
+
+
 def kquant_dense_workload(args, dev):
     """The dense 20B-class pass in the Q4_K_M mix: Q4_K QKV, out and up, Q6_K down."""
     return dense_workload(args, dev, cfg=6)
@@ -779,7 +848,7 @@ def kquant_dense_workload(args, dev):
 
 WORKLOADS = {"dense20b": dense_workload, "q4_0_4096": q4_0_workload, "moe_mxfp4": moe_workload,
              "ffn_streamed": ffn_streamed_workload, "q8_0_256": q8_0_small_workload,
-             "q4_k_m_dense20b": kquant_dense_workload}
+             "q4_k_m_dense20b": kquant_dense_workload, "dense20b_batch": dense_batch_workload}
 
 
 # --- entry --------------------------------------------------------------------------
@@ -800,6 +869,8 @@ def main(argv=None):
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--block-rows", type=int, default=0, help="block_rows for the MoE workload")
+    p.add_argument("--batch", type=int, default=4, help="tokens per step of dense20b_batch")
+    p.add_argument("--kquant", action="store_true", help="dense20b_batch in the Q4_K_M mix")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a 256 MiB device-to-device copy (a kernel of known traffic, to scale HBM counters)")
     args = p.parse_args(argv)

@@ -153,6 +153,23 @@ int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
 
 /* Input transforms (qgemv_rows_op, chain steps) and output transforms
  * (qgemv_rows_op). */
+/* A small batch: y_t = W[row_start:row_end] . x_t for n_tok tokens t, with
+ * every weight block read from memory and decoded once per pass for several
+ * tokens (neurostream README, "What the numbers taught us": tokens that share
+ * one pass over the weights cost about one token's weight traffic).  Token
+ * t's x is the k floats at x + t * x_stride, its y the row_end - row_start
+ * floats at y + t * y_stride (device pointers; y_stride >= row_end -
+ * row_start when n_tok > 1, so outputs never overlap; x_stride >= 0).  A
+ * pass takes four tokens while the row fits one 32-weight column per lane in
+ * at most 8 waves (Q8_0, Q4_K, Q6_K: k <= 16384), else two while it fits one
+ * column in 12 waves or two columns in 8 (every format up to k = 32768),
+ * else one; the weights are read once per pass.  Each
+ * y_t has the bits qgemv_rows gives for x_t alone.  n_tok = 0 or an empty
+ * window does nothing; block_rows as in qgemv_rows. */
+int qgemv_rows_batch(const qg_matrix *w, int64_t row_start, int64_t row_end,
+                     const float *x, int64_t x_stride, int32_t n_tok, float *y,
+                     int64_t y_stride, int64_t block_rows, qg_stream_t stream);
+
 enum qg_in_op { QG_IN_X = 0, QG_IN_RMS = 1, QG_IN_GELU_RMS = 2, QG_IN_SILU_MUL = 3 };
 enum qg_out_op { QG_OUT_Y = 0, QG_OUT_GELU = 1 };
 

@@ -82,6 +82,7 @@ def lib():
         "qgemv_weight_bytes": ([_i32, _i64, _i64], _i64),
         "qgemv_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
+        "qgemv_rows_batch": ([P(qg_matrix), _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i64, _vp], ctypes.c_int),
         "qgemv_rows_op": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _i64, _vp],
                           ctypes.c_int),
         "qgemv_expert_windows": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _i64, _vp, _i64, _vp],
@@ -219,6 +220,22 @@ def qgemv_rows_op(w: Matrix, row_start: int, row_end: int, x, y, in_op: int = 0,
     _check(lib().qgemv_rows_op(ctypes.byref(m), row_start, row_end, _f32(x, w.k, "x"), x2p, int(in_op),
                                float(eps), int(out_op), _f32(y, n, "y"), block_rows, _stream(stream)),
            "qgemv_rows_op")
+
+
+def qgemv_rows_batch(w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 0, stream=None) -> None:
+    """y[t] = W[row_start:row_end] . x[t] for every token t: ``x`` is (n_tok, >= k)
+    and ``y`` (n_tok, >= row_end - row_start), float32 with unit column stride."""
+    m = w.c()
+    n = max(row_end - row_start, 0)
+    if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
+        raise ValueError("x and y must be (n_tok, ...) with the same n_tok")
+    if x.stride(1) != 1 or y.stride(1) != 1 or x.shape[1] < w.k or y.shape[1] < n:
+        raise ValueError("rows of x (k floats) and y (one per output row) must be contiguous")
+    nt = x.shape[0]
+    _f32(x, 0, "x")
+    _f32(y, 0, "y")
+    _check(lib().qgemv_rows_batch(ctypes.byref(m), row_start, row_end, _ptr(x), x.stride(0), nt, _ptr(y),
+                                  y.stride(0), block_rows, _stream(stream)), "qgemv_rows_batch")
 
 
 def qgemv_windows(windows: Sequence[Window], block_rows: int = 0, stream=None, fmt=None, k=None) -> None:

@@ -57,6 +57,8 @@ extern template GemvFn pick_op<kOpRms>(int32_t, Shape);
 extern template GemvFn pick_op<kOpRmsGelu>(int32_t, Shape);
 extern template GemvFn pick_op<kOpSilu>(int32_t, Shape);
 extern template GemvFn pick_op<kOpGelu>(int32_t, Shape);
+extern template GemvFn pick_batch<2>(int32_t, Shape);
+extern template GemvFn pick_batch<4>(int32_t, Shape);
 }  // namespace qgemv_detail
 
 namespace {
@@ -842,10 +844,11 @@ GemvFn pick(int32_t fmt, Shape s, int32_t in_op, int32_t out_op) {
 
 // in_op / out_op / eps: the fused transforms (QG_IN_X, QG_OUT_Y: none); x2[i]
 // is window i's SiLU multiplier (x2 may be null when in_op is not
-// QG_IN_SILU_MUL).
+// QG_IN_SILU_MUL).  nt > 1: nt tokens (2 or 4, no transform), token t's x at
+// win.x + t x_stride and its y at win.y + t y_stride.
 int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
                 hipStream_t stream, int32_t in_op = QG_IN_X, float eps = 0.0f, int32_t out_op = QG_OUT_Y,
-                const float *const *x2 = nullptr) {
+                const float *const *x2 = nullptr, int nt = 1, int64_t x_stride = 0, int64_t y_stride = 0) {
   Shape s;
   int rc = team_shape(fmt, k, &s);
   if (rc) return rc;
@@ -892,8 +895,13 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   a.in_op = in_op;
   a.out_op = out_op;
   a.eps = eps;
+  a.x_stride = x_stride;
+  a.y_stride = y_stride;
   const int64_t teams = std::min<int64_t>(teams_max, tiles);
-  const GemvFn fn = pick(fmt, s, in_op, out_op);
+  const GemvFn fn = nt == 1 ? pick(fmt, s, in_op, out_op)
+                    : nt == 2 && in_op == QG_IN_X && out_op == QG_OUT_Y ? pick_batch<2>(fmt, s)
+                    : nt == 4 && in_op == QG_IN_X && out_op == QG_OUT_Y ? pick_batch<4>(fmt, s)
+                                                                        : nullptr;
   if (!fn) return QG_E_ARG;
   hipLaunchKernelGGL(fn, dim3((unsigned)teams), dim3(64 * s.wt), 0, stream, a);
   QG_HIP(hipGetLastError());
@@ -978,6 +986,32 @@ int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const flo
   if (!x || !y) return QG_E_NULL;
   qg_window win = {w->data, w->n_rows, row_start, row_end, x, y};
   return launch_gemv(w->fmt, w->k, &win, 1, block_rows, stream);
+}
+
+int qgemv_rows_batch(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, int64_t x_stride,
+                     int32_t n_tok, float *y, int64_t y_stride, int64_t block_rows, qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  const int64_t n = row_end - row_start;
+  if (block_rows < 0 || n_tok < 0 || x_stride < 0 || (n_tok > 1 && y_stride < n)) return QG_E_ARG;
+  if (n == 0 || n_tok == 0) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  Shape s;
+  if ((rc = team_shape(w->fmt, w->k, &s))) return rc;
+  qg_window win = {w->data, w->n_rows, row_start, row_end, nullptr, nullptr};
+  // passes of four tokens (two, one) while the team shape allows
+  for (int32_t t = 0; t < n_tok;) {
+    const int32_t left = n_tok - t;
+    const int nt = left >= 4 && s.wt <= batch_max_wt(4, s.c) ? 4 : left >= 2 && s.wt <= batch_max_wt(2, s.c) ? 2 : 1;
+    win.x = x + (int64_t)t * x_stride;
+    win.y = y + (int64_t)t * y_stride;
+    if ((rc = launch_gemv(w->fmt, w->k, &win, 1, block_rows, stream, QG_IN_X, 0.0f, QG_OUT_Y, nullptr, nt,
+                          x_stride, y_stride)))
+      return rc;
+    t += nt;
+  }
+  return QG_OK;
 }
 
 int qgemv_rows_op(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, const float *x2,

@@ -1,8 +1,9 @@
 // qgemv_impl.h -- gfx950 GEMV kernel templates shared by libqgemv.so's
 // translation units: the block formats, the fused row dot, the GEMV kernel and
 // its launch-shape picker.  Each fused-transform variant of the GEMV kernel is
-// instantiated in a translation unit of its own (gemv_op*.hip), so the library
-// builds in parallel; qgemv.hip holds the chain kernel and the C ABI.
+// instantiated in a translation unit of its own (gemv_op*.hip, and the
+// several-token kernels in gemv_batch.hip), so the library builds in
+// parallel; qgemv.hip holds the chain kernel and the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -149,8 +150,11 @@ template <> struct Fmt<QG_Q4_K> {
     for (int i = 0; i < 8; ++i) q[i] &= mask;
     return (s & 1) ? 0.0625f : 1.0f;
   }
-  __device__ static inline float dot(const uint8_t *blk, int s, const float (&x)[32], const float (&xs)[2],
-                                     float acc) {
+  // res[t] = acc[t] + this sub-block's dot with token t's inputs; the codes
+  // are read and masked once for all NT tokens.
+  template <int NT>
+  __device__ static inline void dot(const uint8_t *blk, int s, const float (&x)[NT][32], const float (&xs)[NT][2],
+                                    const float (&acc)[NT], float (&res)[NT]) {
     uint32_t hd;
     __builtin_memcpy(&hd, blk, 4);
     int sc, m;
@@ -159,18 +163,21 @@ template <> struct Fmt<QG_Q4_K> {
     __builtin_memcpy(q, blk + 16 + 32 * (s >> 1), 32);
     // codes of bytes 0 and 2 (then 1 and 3) of a word as two fp16 subnormals
     const uint32_t mask = (s & 1) ? 0x00F000F0u : 0x000F000Fu;
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t a = q[i] & mask, b = (q[i] >> 8) & mask;
-      p[0] = fmaf(h16_lo(a), x[4 * i + 0], p[0]);
-      p[1] = fmaf(h16_lo(b), x[4 * i + 1], p[1]);
-      p[2] = fmaf(h16_hi(a), x[4 * i + 2], p[2]);
-      p[3] = fmaf(h16_hi(b), x[4 * i + 3], p[3]);
-    }
     const float f = (s & 1) ? 0x1p20f : 0x1p24f;
-    acc = fmaf(half_bits(hd) * (float)sc * f, (p[0] + p[1]) + (p[2] + p[3]), acc);
-    return fmaf(-(half_bits(hd >> 16) * (float)m), xs[0] + xs[1], acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = q[i] & mask, b = (q[i] >> 8) & mask;
+        p[0] = fmaf(h16_lo(a), x[t][4 * i + 0], p[0]);
+        p[1] = fmaf(h16_lo(b), x[t][4 * i + 1], p[1]);
+        p[2] = fmaf(h16_hi(a), x[t][4 * i + 2], p[2]);
+        p[3] = fmaf(h16_hi(b), x[t][4 * i + 3], p[3]);
+      }
+      const float r = fmaf(half_bits(hd) * (float)sc * f, (p[0] + p[1]) + (p[2] + p[3]), acc[t]);
+      res[t] = fmaf(-(half_bits(hd >> 16) * (float)m), xs[t][0] + xs[t][1], r);
+    }
   }
   // The 32 weights of sub-block s, each rounded once: d sc q and dmin m are
   // exact in fp32 (so is d sc / 16 times 16 q).
@@ -212,21 +219,26 @@ template <> struct Fmt<QG_Q6_K> {
     for (int w = 0; w < 8; ++w)
       q[w] = ((lo[w] >> s4) & 0x0F0F0F0Fu) | (__builtin_amdgcn_alignbit(hi[w], hi[w], rot) & 0x30303030u);
   }
-  __device__ static inline float dot(const uint8_t *blk, int u, const float (&x)[32], const float (&xs)[2],
-                                     float acc) {
+  template <int NT>
+  __device__ static inline void dot(const uint8_t *blk, int u, const float (&x)[NT][32], const float (&xs)[NT][2],
+                                    const float (&acc)[NT], float (&res)[NT]) {
     uint32_t q[8];
     codes(blk, u, q);
     const float sa = (float)(int8_t)blk[192 + 2 * u], sb = (float)(int8_t)blk[193 + 2 * u];
     uint32_t hd = 0;
     __builtin_memcpy(&hd, blk + 208, 2);
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int w = 0; w < 8; ++w)
+    for (int t = 0; t < NT; ++t) {
+      float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        p[2 * (w >> 2) + (k & 1)] = fmaf((float)((q[w] >> (8 * k)) & 0xffu), x[4 * w + k], p[2 * (w >> 2) + (k & 1)]);
-    const float pa = fmaf(-32.0f, xs[0], p[0] + p[1]), pb = fmaf(-32.0f, xs[1], p[2] + p[3]);
-    return fmaf(half_bits(hd), fmaf(sa, pa, sb * pb), acc);
+      for (int w = 0; w < 8; ++w)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          p[2 * (w >> 2) + (k & 1)] =
+              fmaf((float)((q[w] >> (8 * k)) & 0xffu), x[t][4 * w + k], p[2 * (w >> 2) + (k & 1)]);
+      const float pa = fmaf(-32.0f, xs[t][0], p[0] + p[1]), pb = fmaf(-32.0f, xs[t][1], p[2] + p[3]);
+      res[t] = fmaf(half_bits(hd), fmaf(sa, pa, sb * pb), acc[t]);
+    }
   }
   // The 32 weights of unit u, each rounded once: d scale is exact in fp32.
   __device__ static inline void dequant(const uint8_t *blk, int u, float w[32]) {
@@ -265,6 +277,9 @@ struct GemvArgs {
   int32_t in_op;   // QG_IN_X, QG_IN_RMS or QG_IN_SILU_MUL: applied as x is loaded
   int32_t out_op;  // QG_OUT_Y or QG_OUT_GELU: applied as y is stored
   float eps;       // of QG_IN_RMS
+  // Several tokens per launch (NT > 1): token t's x at win.x + t x_stride,
+  // its y at win.y + t y_stride.
+  int64_t x_stride, y_stride;
 };
 
 // Sum over the 64 lanes of a wave in a fixed order (DPP row shifts, then row
@@ -293,23 +308,29 @@ __device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * erfcf(-t 
 // silu(g) * u, as qgemv_silu_mul computes it.
 __device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// One wave's partial sum for one staged row: lane l dots blocks l + 64c
-// (c < C) of the wave's slice, staged at byte `ph` of `sb`, with its
-// registered activations.  Fixed order: four FMA chains per block combined
-// as (p0 + p1) + (p2 + p3), the block scale applied once, blocks in c order.
-template <int FMT, int C>
-__device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane, int slice_n,
-                                             const float (&xr)[C][32], const float (&xs)[C][2]) {
+// One wave's partial sums for one staged row and NT tokens: lane l dots
+// blocks l + 64c (c < C) of the wave's slice, staged at byte `ph` of `sb`,
+// with each token's registered activations, decoding every block once.
+// Fixed order per token: four FMA chains per block combined as
+// (p0 + p1) + (p2 + p3), the block scale applied once, blocks in c order --
+// the same for any NT, so a token's sum does not depend on its batch.
+template <int FMT, int C, int NT>
+__device__ __forceinline__ void row_partial(const uint8_t *sb, int ph, int lane, int slice_n,
+                                            const float (&xr)[C][NT][32], const float (&xs)[C][NT][2],
+                                            float (&s)[NT]) {
   using F = Fmt<FMT>;
-  float s = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) s[t] = 0.0f;
   if constexpr (F::kUnits > 1) {
     // K-quants: lane l's unit b = l + 64 c is sub-block b % 8 of the slice's
     // super-block b / 8.
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int b = lane + 64 * c;
-      const float acc = F::dot(sb + ph + F::kBytes * (b >> 3), b & 7, xr[c], xs[c], s);
-      s = b < slice_n ? acc : s;
+      float acc[NT];
+      F::template dot<NT>(sb + ph + F::kBytes * (b >> 3), b & 7, xr[c], xs[c], s, acc);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s[t] = b < slice_n ? acc[t] : s[t];
     }
   } else {
 #pragma unroll
@@ -323,14 +344,26 @@ __device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane
       __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
       float u[32];
       F::decode(q, u);
-      float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][e], p[e & 3]);
-      const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s);
-      s = b < slice_n ? blk_acc : s;
+      for (int t = 0; t < NT; ++t) {
+        float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) p[e & 3] = fmaf(u[e], xr[c][t][e], p[e & 3]);
+        const float blk_acc = F::fma_acc(F::scale(sbits), (p[0] + p[1]) + (p[2] + p[3]), s[t]);
+        s[t] = b < slice_n ? blk_acc : s[t];
+      }
     }
   }
-  return s;
+}
+
+// One token's partial sum (the chain kernel's form).
+template <int FMT, int C>
+__device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane, int slice_n,
+                                             const float (&xr)[C][32], const float (&xs)[C][2]) {
+  float s[1];
+  row_partial<FMT, C, 1>(sb, ph, lane, slice_n, reinterpret_cast<const float (&)[C][1][32]>(xr),
+                         reinterpret_cast<const float (&)[C][1][2]>(xs), s);
+  return s[0];
 }
 
 // The unit input sums row_partial takes for the 32-weight formats, which use none.
@@ -403,14 +436,18 @@ __host__ __device__ constexpr int op_in(int op) {
 }
 __host__ __device__ constexpr bool op_gelu(int op) { return op == kOpRmsGelu || op == kOpGelu; }
 
-template <int FMT, int WT, int C, int OP>
+// NT > 1: NT tokens per launch (a small batch): every block is staged and
+// decoded once and dotted with each token's activations, in the one-token
+// order, so each token's y has the bits of a one-token launch.
+template <int FMT, int WT, int C, int OP, int NT = 1>
 __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
+  static_assert(NT == 1 || OP == kOpNone, "fused transforms take one token");
   using G = Geo<FMT, C>;
   constexpr int V = G::V, SLOT = G::SLOT;
   constexpr int NB = gemv_in_flight(FMT, WT), NS = NB + 1;
   constexpr int SB = 64 * C;  // blocks per slice
   __shared__ __attribute__((aligned(16))) uint8_t ring[WT][NS][SLOT];
-  __shared__ float red[2][WT][kGemvTileRows];
+  __shared__ float red[2][WT][NT * kGemvTileRows];
   __shared__ float ssq[WT * C];
 
   const int lane = threadIdx.x & 63;
@@ -493,8 +530,8 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   // consecutive inputs per lane in order, the lanes of a 64-column run by
   // wave_sum63, the runs in column order -- the team's waves cover every
   // column, so no extra read), then one scale per input.
-  float xr[C][32];
-  float xs[C][2];  // K-quants: the sums of each unit's first and last 16 inputs
+  float xr[C][NT][32];
+  float xs[C][NT][2];  // K-quants: the sums of each unit's first and last 16 inputs
   constexpr int in_op = op_in(OP);
   auto load_x = [&](const float *x, const float *x2) {
 #pragma unroll
@@ -502,22 +539,26 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       const int j = slice_b0 + lane + 64 * c;
       const int jj = min(j, nb - 1);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float4 v;
-        __builtin_memcpy(&v, x + 32 * jj + 4 * q, 16);
-        if constexpr (in_op == QG_IN_SILU_MUL) {
-          float4 u;
-          __builtin_memcpy(&u, x2 + 32 * jj + 4 * q, 16);
-          v.x = silu_times(v.x, u.x);
-          v.y = silu_times(v.y, u.y);
-          v.z = silu_times(v.z, u.z);
-          v.w = silu_times(v.w, u.w);
+      for (int t = 0; t < NT; ++t) {
+        const float *xt = NT == 1 ? x : x + t * a.x_stride;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float4 v;
+          __builtin_memcpy(&v, xt + 32 * jj + 4 * q, 16);
+          if constexpr (in_op == QG_IN_SILU_MUL) {
+            float4 u;
+            __builtin_memcpy(&u, x2 + 32 * jj + 4 * q, 16);
+            v.x = silu_times(v.x, u.x);
+            v.y = silu_times(v.y, u.y);
+            v.z = silu_times(v.z, u.z);
+            v.w = silu_times(v.w, u.w);
+          }
+          const bool ok = j < nb;
+          xr[c][t][4 * q + 0] = ok ? v.x : 0.0f;
+          xr[c][t][4 * q + 1] = ok ? v.y : 0.0f;
+          xr[c][t][4 * q + 2] = ok ? v.z : 0.0f;
+          xr[c][t][4 * q + 3] = ok ? v.w : 0.0f;
         }
-        const bool ok = j < nb;
-        xr[c][4 * q + 0] = ok ? v.x : 0.0f;
-        xr[c][4 * q + 1] = ok ? v.y : 0.0f;
-        xr[c][4 * q + 2] = ok ? v.z : 0.0f;
-        xr[c][4 * q + 3] = ok ? v.w : 0.0f;
       }
     }
     if constexpr (in_op == QG_IN_RMS) {
@@ -525,7 +566,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       for (int c = 0; c < C; ++c) {
         float ss = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) ss = fmaf(xr[c][e], xr[c][e], ss);
+        for (int e = 0; e < 32; ++e) ss = fmaf(xr[c][0][e], xr[c][0][e], ss);
         ss = wave_sum63(ss);
         if (lane == 63) ssq[C * wave + c] = ss;
       }
@@ -537,7 +578,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
 #pragma unroll
       for (int c = 0; c < C; ++c)
 #pragma unroll
-        for (int e = 0; e < 32; ++e) xr[c][e] *= inv;
+        for (int e = 0; e < 32; ++e) xr[c][0][e] *= inv;
       __syncthreads();  // ssq is read before a later window rewrites it
     }
     if constexpr (Fmt<FMT>::kUnits > 1) {
@@ -547,14 +588,17 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
 #pragma clang fp contract(off)
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          lo += xr[c][e];
-          hi += xr[c][16 + e];
+        for (int t = 0; t < NT; ++t) {
+          float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            lo += xr[c][t][e];
+            hi += xr[c][t][16 + e];
+          }
+          xs[c][t][0] = lo;
+          xs[c][t][1] = hi;
         }
-        xs[c][0] = lo;
-        xs[c][1] = hi;
       }
     }
   };
@@ -605,10 +649,11 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     // (ph0 + i * rb) mod 16 within its first granule.
     const uint32_t ph0 = (uint32_t)((uintptr_t)(CW.base + cur.r0 * rb) & 15);
     const uint32_t rb16 = (uint32_t)(rb & 15);
-    float acc[kGemvTileRows];
+    float acc[NT][kGemvTileRows];
 #pragma unroll
     for (int i = 0; i < kGemvTileRows; ++i) {
-      acc[i] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][i] = 0.0f;
       if (i < nrows) {
         // The slot NB ahead held the previous row, whose LDS reads are done.
         int s2 = slot + NB;
@@ -619,7 +664,10 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
         wait_vmcnt<V * NB>();  // this row's copies have landed
         const uint8_t *sb = &ring[wave][slot][0];
         const int ph = (int)((ph0 + (uint32_t)i * rb16) & 15);
-        acc[i] = wave_sum63(row_partial<FMT, C>(sb, ph, lane, slice_n, xr, xs));
+        float part[NT];
+        row_partial<FMT, C, NT>(sb, ph, lane, slice_n, xr, xs, part);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][i] = wave_sum63(part[t]);
         slot = slot + 1 == NS ? 0 : slot + 1;
       }
     }
@@ -628,20 +676,35 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     if (WT == 1) {
       if (lane == 63) {
 #pragma unroll
-        for (int i = 0; i < kGemvTileRows; ++i)
-          if (i < nrows) yt[i] = gelu_out ? gelu_erf(acc[i]) : acc[i];
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < kGemvTileRows; ++i)
+            if (i < nrows) yt[t * a.y_stride + i] = gelu_out ? gelu_erf(acc[t][i]) : acc[t][i];
       }
     } else {
       if (lane == 63) {
 #pragma unroll
-        for (int i = 0; i < kGemvTileRows; ++i) red[parity][wave][i] = acc[i];
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < kGemvTileRows; ++i) red[parity][wave][t * kGemvTileRows + i] = acc[t][i];
       }
       __syncthreads();
-      if ((int)threadIdx.x < nrows) {
-        float s = red[parity][0][threadIdx.x];
+      if constexpr (NT == 1) {
+        if ((int)threadIdx.x < nrows) {
+          float s = red[parity][0][threadIdx.x];
 #pragma unroll
-        for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
-        yt[threadIdx.x] = gelu_out ? gelu_erf(s) : s;
+          for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
+          yt[threadIdx.x] = gelu_out ? gelu_erf(s) : s;
+        }
+      } else {
+        // thread t * kGemvTileRows + i stores token t's row i (64 WT >= 8 NT)
+        const int t = (int)threadIdx.x / kGemvTileRows, i = (int)threadIdx.x % kGemvTileRows;
+        if (t < NT && i < nrows) {
+          float s = red[parity][0][threadIdx.x];
+#pragma unroll
+          for (int v = 1; v < WT; ++v) s += red[parity][v][threadIdx.x];
+          yt[t * a.y_stride + i] = s;
+        }
       }
       parity ^= 1;
     }
@@ -669,6 +732,42 @@ template <int FMT, int OP>
 GemvFn pick_fmt(Shape s) {
   if (s.c == 1) return pick_wt<FMT, 1, OP>(s.wt, std::make_integer_sequence<int, kMaxWT>{});
   return pick_wt<FMT, 2, OP>(s.wt, std::make_integer_sequence<int, kMaxWT>{});
+}
+
+// Several tokens per launch, sized by the activation registers (32 per token
+// and column): four tokens with one column per lane and teams of at most 8
+// waves (two waves per SIMD), two tokens with one column and any team or two
+// columns and at most 8 waves; 0 = no kernel.
+__host__ __device__ constexpr int batch_max_wt(int nt, int c) {
+  return nt == 4 ? (c == 1 ? 8 : 0) : nt == 2 ? (c == 1 ? kMaxWT : 8) : kMaxWT;
+}
+
+template <int FMT, int C, int NT, int... WT>
+GemvFn pick_wt_batch(int wt, std::integer_sequence<int, WT...>) {
+  GemvFn fn = nullptr;
+  ((wt == WT + 1 ? (fn = gemv_kernel<FMT, WT + 1, C, kOpNone, NT>, 0) : 0), ...);
+  return fn;
+}
+
+template <int FMT, int NT>
+GemvFn pick_fmt_batch(Shape s) {
+  constexpr int M1 = batch_max_wt(NT, 1), M2 = batch_max_wt(NT, 2);
+  if (s.c == 1 && s.wt <= M1) return pick_wt_batch<FMT, 1, NT>(s.wt, std::make_integer_sequence<int, M1>{});
+  if constexpr (M2 > 0) {
+    if (s.c == 2 && s.wt <= M2) return pick_wt_batch<FMT, 2, NT>(s.wt, std::make_integer_sequence<int, M2>{});
+  }
+  return nullptr;
+}
+
+template <int NT>
+GemvFn pick_batch(int32_t fmt, Shape s) {
+  switch (fmt) {
+    case QG_Q8_0: return pick_fmt_batch<QG_Q8_0, NT>(s);
+    case QG_Q4_0: return pick_fmt_batch<QG_Q4_0, NT>(s);
+    case QG_Q4_K: return pick_fmt_batch<QG_Q4_K, NT>(s);
+    case QG_Q6_K: return pick_fmt_batch<QG_Q6_K, NT>(s);
+    default: return pick_fmt_batch<QG_MXFP4, NT>(s);
+  }
 }
 
 template <int OP>
