@@ -892,6 +892,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   a.block_rows = B;
   a.tile_rows = tile_rows;
   a.n_tiles = (int32_t)tiles;
+  a.tiles_per_block = (int32_t)tpb;
   a.in_op = in_op;
   a.out_op = out_op;
   a.eps = eps;

@@ -274,6 +274,7 @@ struct GemvArgs {
   int64_t row_bytes;
   int64_t block_rows;  // > 0 (the host replaces 0 by a bound above every window)
   int32_t n_win, nb, tile_rows, n_tiles;
+  int32_t tiles_per_block;  // ceil(block_rows / tile_rows)
   int32_t in_op;   // QG_IN_X, QG_IN_RMS or QG_IN_SILU_MUL: applied as x is loaded
   int32_t out_op;  // QG_OUT_Y or QG_OUT_GELU: applied as y is stored
   float eps;       // of QG_IN_RMS
@@ -460,13 +461,16 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   const int64_t slice_off = (int64_t)(slice_b0 / Fmt<FMT>::kUnits) * Fmt<FMT>::kBytes;
   const uint32_t slice_len = (uint32_t)(slice_n / Fmt<FMT>::kUnits) * Fmt<FMT>::kBytes;
   const int T = gridDim.x;
-  if ((int)blockIdx.x >= a.n_tiles) return;
 
   // Kernel-argument fields used in the loop are read once into registers, and
-  // a window's fields again only when a cursor enters the next window.
+  // a window's fields again only when a cursor enters the next window.  The
+  // first window's and the tiling fields are all read before any is used, so
+  // the launch waits on one round trip to the argument buffer, not a chain.
+  const int n_tiles = a.n_tiles;
   const int64_t B = a.block_rows;
   const int TR = a.tile_rows;
-  const int tpb = (int)((B + TR - 1) / TR);
+  const int tpb = a.tiles_per_block;
+  const float eps = a.eps;
   struct Win {
     int w, t0, t1;  // window index, its tiles [t0, t1)
     int64_t row_start, row_end;
@@ -574,7 +578,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       float tot = 0.0f;
 #pragma unroll
       for (int v = 0; v < C * WT; ++v) tot += ssq[v];
-      const float inv = 1.0f / sqrtf(tot / (float)(32 * nb) + a.eps);
+      const float inv = 1.0f / sqrtf(tot / (float)(32 * nb) + eps);
 #pragma unroll
       for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -609,6 +613,11 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   // a slot no computation reads, which keeps one fixed count of loads per row.
   Win CW, FW;
   load_win(0, CW);
+  // An empty statement consuming those fields keeps the compiler from
+  // sinking their loads past the branches below (one wait, not four).
+  asm volatile("" ::"s"(n_tiles), "s"(B), "s"(TR), "s"(tpb), "s"(eps), "s"(T), "s"(CW.t0), "s"(CW.t1),
+               "s"(CW.row_start), "s"(CW.row_end), "s"(CW.base), "s"(CW.x), "s"(CW.x2), "s"(CW.y));
+  if ((int)blockIdx.x >= n_tiles) return;
   Tile cur, F;
   locate(blockIdx.x, CW, cur);
   FW = CW;
@@ -622,7 +631,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       fp += rb;
       return;
     }
-    if (F.t + T < a.n_tiles) {
+    if (F.t + T < n_tiles) {
       locate(F.t + T, FW, F);
       fp = FW.base + F.r0 * rb;
       f_left = F.nrows;
@@ -708,7 +717,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       }
       parity ^= 1;
     }
-    if (cur.t + T >= a.n_tiles) break;
+    if (cur.t + T >= n_tiles) break;
     locate(cur.t + T, CW, cur);
   }
   // The ring's last copies (re-reads past the end) must land before the
