@@ -623,7 +623,10 @@ def moe_workload(args, dev):
     """MXFP4 MoE expert GEMV: stacked (128, 2880, 2880) gate/up/down, 4 of 128
     experts per token (seeded uniform top-4), 64 tokens.  Per token: one grid
     over the 8 gate/up windows of the selected experts, SiLU*up, one grid over
-    the 4 down windows."""
+    the 4 down windows, and the router-weighted combine of the 4 expert
+    outputs (seeded weights).  (SiLU*up fused into the down grid's x-load,
+    qgemv_expert_windows_op, is slower here: every one of the ~1,400 teams
+    of that small grid evaluates it for its whole input slice.)"""
     import torch
     import quantized_gemv_gguf_amd as q
     c = synth.CONFIGS[4]
@@ -635,7 +638,9 @@ def moe_workload(args, dev):
     xs = torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(4, 100 + t)) for t in range(c["tokens"])])).to(dev)
     gu = torch.empty(2 * ns * out, dtype=torch.float32, device=dev)
     h = torch.empty(ns * out, dtype=torch.float32, device=dev)
-    y = torch.empty((c["tokens"], ns * out), dtype=torch.float32, device=dev)
+    ye = torch.empty(ns * out, dtype=torch.float32, device=dev)
+    y = torch.empty((c["tokens"], out), dtype=torch.float32, device=dev)
+    wts = torch.from_numpy(synth.router_weights(c["tokens"], ns, synth.seed_of(4, 9))).to(dev)
     L = q.lib()
     st = torch.cuda.current_stream().cuda_stream
     m2 = (q.qg_matrix * 2)(mats[0].c(), mats[1].c())
@@ -647,7 +652,8 @@ def moe_workload(args, dev):
         t = t % c["tokens"]
         rc = L.qgemv_expert_windows(m2, 2, E, idarr[t], ns, xs[t].data_ptr(), 0, gu.data_ptr(), B, st)
         rc |= L.qgemv_silu_mul(gu.data_ptr(), gu.data_ptr() + 4 * ns * out, h.data_ptr(), ns * out, st)
-        rc |= L.qgemv_expert_windows(m1, 1, E, idarr[t], ns, h.data_ptr(), out, y[t].data_ptr(), B, st)
+        rc |= L.qgemv_expert_windows(m1, 1, E, idarr[t], ns, h.data_ptr(), out, ye.data_ptr(), B, st)
+        rc |= L.qgemv_combine(ye.data_ptr(), out, ns, wts[t].data_ptr(), out, y[t].data_ptr(), st)
         assert rc == 0
 
     for t in range(args.warmup):
@@ -660,6 +666,7 @@ def moe_workload(args, dev):
             "bytes_per_token": per_tok,
             "config": {"workload": c["name"], "format": "MXFP4", "n_expert": E, "out": out, "k": k,
                        "experts_per_token": ns, "tokens": n, "block_rows": B,
+                       "launches_per_token": "gate/up grid, SiLU*up, down grid, combine",
                        "resident_bytes": 3 * q.qgemv_weight_bytes(q.MXFP4, rows, k)}}
 
 

@@ -217,8 +217,35 @@ int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert,
 /* h[i] = silu(g[i]) * u[i], silu(v) = v / (1 + exp(-v)), fp32, device
  * pointers, n >= 0 (the SwiGLU activation between the row-contiguous gate/up
  * and down phases: neurostream README, "How it works"; run on the GPU as in
- * hipfire PR, "Design notes", silu_mul). */
+ * hipfire PR, "Design notes", silu_mul).  exp and the division use the
+ * hardware exp2 and reciprocal: within about (|g| + 4) * 2^-24 of the exact
+ * value, relative; the fused QG_IN_SILU_MUL loads give the same bits. */
 int qgemv_silu_mul(const float *g, const float *u, float *h, int64_t n, qg_stream_t stream);
+
+/* As qgemv_expert_windows, with qgemv_rows_op's fused transforms applied per
+ * window: selected expert s reads x + s * x_stride and, for QG_IN_SILU_MUL,
+ * x2 + s * x_stride.  With the gate outputs as x and the up outputs as x2 the
+ * down grid takes silu(gate) * up as it loads it, so an MoE token is two
+ * grids with no elementwise launch between them (neurostream README, "What
+ * the numbers taught us": drains and small launches, not bytes, set the time
+ * per step; hipfire PR, "Design notes": the fused SwiGLU GEMV).  in_op,
+ * out_op, eps and their errors as qgemv_rows_op (QG_IN_RMS needs k <= 32768
+ * and normalises each window's own x).  Results equal the separate calls'
+ * bits. */
+int qgemv_expert_windows_op(const qg_matrix *mats, int32_t n_mat, int64_t n_expert,
+                            const int32_t *ids, int32_t n_sel, const float *x,
+                            const float *x2, int64_t x_stride, int32_t in_op, float eps,
+                            int32_t out_op, float *y, int64_t block_rows, qg_stream_t stream);
+
+/* Router-weighted combine of the selected experts' outputs: out[i] =
+ * sum_{s < n_sel} w[s] * y[s * y_stride + i], one fp32 fma per term in s
+ * order (neurostream README, "How it works": the router names the active
+ * experts and their outputs are mixed back into one vector).  y (n_sel
+ * vectors of n floats, y_stride >= n when n_sel > 1), w (n_sel weights) and
+ * out (n floats, not overlapping y) are device pointers.  n_sel = 0 writes
+ * zeros; n = 0 does nothing. */
+int qgemv_combine(const float *y, int64_t y_stride, int32_t n_sel, const float *w, int64_t n,
+                  float *out, qg_stream_t stream);
 
 /* out = rms(act(v)), act = identity (gelu = 0) or exact erf GELU (gelu = 1),
  * rms(t) = t / sqrt(mean(t^2) + eps), no gain; fp32, device pointers, n >= 1,

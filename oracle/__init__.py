@@ -16,7 +16,8 @@ Functions (each follows the passage cited in ``oracle.c``):
 * ``gemv_rows(fmt, w, n_rows, k, r0, r1, x)`` -> ``(y, a)`` in fp64, with
   ``y[j] = sum_i W[r0+j, i] x[i]`` (RAMforge README "Milestone 6", matrix
   layout) and ``a[j] = sum_i |W[r0+j, i] x[i]|``.
-* ``silu_mul(g, u)`` and ``rms_carry(v, eps, gelu)`` in fp64.
+* ``silu_mul(g, u)``, ``rms_carry(v, eps, gelu)`` and ``combine(y, w)`` (the
+  router-weighted sum of expert outputs) in fp64.
 """
 from __future__ import annotations
 
@@ -72,6 +73,8 @@ def load(path: str | None = None):
     lib.orc_silu_mul.restype = None
     lib.orc_rms_carry.argtypes = [vp, vp, i64, ctypes.c_double, i32]
     lib.orc_rms_carry.restype = None
+    lib.orc_combine.argtypes = [vp, i64, i32, vp, i64, vp]
+    lib.orc_combine.restype = None
     if path is None:
         _lib = lib
     return lib
@@ -146,4 +149,14 @@ def rms_carry(v, eps=1e-6, gelu=False, lib=None) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float64)
     out = np.empty_like(v)
     (lib or load()).orc_rms_carry(_ptr(v), _ptr(out), v.size, float(eps), int(bool(gelu)))
+    return out
+
+
+def combine(y, w, lib=None) -> np.ndarray:
+    """out = sum_s w[s] * y[s] in fp64; y is (n_sel, n)."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    n_sel, n = y.shape
+    out = np.empty(n, dtype=np.float64)
+    (lib or load()).orc_combine(_ptr(y), n, n_sel, _ptr(w), n, _ptr(out))
     return out

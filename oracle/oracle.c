@@ -319,3 +319,14 @@ void orc_rms_carry(const double *v, double *out, int64_t n, double eps, int32_t 
   double inv = 1.0 / sqrt(ss / (double)n + eps);
   for (int64_t i = 0; i < n; ++i) out[i] *= inv;
 }
+
+/* Router-weighted combine of per-expert outputs: out[i] = sum_s w[s] *
+ * y[s * y_stride + i], in fp64 (neurostream README, "How it works": the
+ * router's active experts are mixed back into one vector). */
+void orc_combine(const double *y, int64_t y_stride, int32_t n_sel, const double *w, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    double acc = 0.0;
+    for (int32_t s = 0; s < n_sel; ++s) acc += w[s] * y[s * y_stride + i];
+    out[i] = acc;
+  }
+}

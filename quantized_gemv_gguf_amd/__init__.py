@@ -83,6 +83,9 @@ def lib():
         "qgemv_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_rows_batch": ([P(qg_matrix), _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i64, _vp], ctypes.c_int),
+        "qgemv_expert_windows_op": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _vp, _i64, _i32, ctypes.c_float,
+                                     _i32, _vp, _i64, _vp], ctypes.c_int),
+        "qgemv_combine": ([_vp, _i64, _i32, _vp, _i64, _vp, _vp], ctypes.c_int),
         "qgemv_rows_op": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _i64, _vp],
                           ctypes.c_int),
         "qgemv_expert_windows": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _i64, _vp, _i64, _vp],
@@ -257,6 +260,32 @@ def qgemv_expert_windows(mats: Sequence[Matrix], n_expert: int, ids, x, x_stride
     yp = _f32(y, len(mats) * len(ids) * out, "y")
     _check(lib().qgemv_expert_windows(marr, len(mats), n_expert, iarr, len(ids), xp, x_stride, yp,
                                       block_rows, _stream(stream)), "qgemv_expert_windows")
+
+
+def qgemv_expert_windows_op(mats: Sequence[Matrix], n_expert: int, ids, x, x_stride: int, y, in_op: int = 0,
+                            eps: float = 0.0, out_op: int = 0, x2=None, block_rows: int = 0,
+                            stream=None) -> None:
+    """As qgemv_expert_windows with qgemv_rows_op's transforms per window (x2
+    strided like x, for IN_SILU_MUL)."""
+    ids = [int(i) for i in ids]
+    marr = (qg_matrix * len(mats))(*[m.c() for m in mats])
+    iarr = (_i32 * max(len(ids), 1))(*ids)
+    k = mats[0].k if mats else 32
+    out = (mats[0].n_rows // n_expert) if (mats and n_expert > 0) else 0
+    need = k + (len(ids) - 1) * x_stride if ids else 0
+    xp = _f32(x, need, "x")
+    x2p = _f32(x2, need, "x2") if x2 is not None else None
+    yp = _f32(y, len(mats) * len(ids) * out, "y")
+    _check(lib().qgemv_expert_windows_op(marr, len(mats), n_expert, iarr, len(ids), xp, x2p, x_stride, int(in_op),
+                                         float(eps), int(out_op), yp, block_rows, _stream(stream)),
+           "qgemv_expert_windows_op")
+
+
+def qgemv_combine(y, y_stride: int, n_sel: int, w, n: int, out, stream=None) -> None:
+    """out[i] = sum_s w[s] * y[s * y_stride + i] (device tensors)."""
+    yp = _f32(y, (n_sel - 1) * y_stride + n if n_sel > 0 else 0, "y")
+    wp = _f32(w, n_sel, "w")
+    _check(lib().qgemv_combine(yp, y_stride, n_sel, wp, n, _f32(out, n, "out"), _stream(stream)), "qgemv_combine")
 
 
 def qgemv_mapped_rows(w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 0,

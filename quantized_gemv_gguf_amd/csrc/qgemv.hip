@@ -102,7 +102,19 @@ __global__ void silu_mul_kernel(const float *g, const float *u, float *h, int64_
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
     const float v = g[i];
-    h[i] = v / (1.0f + expf(-v)) * u[i];
+    h[i] = silu_times(v, u[i]);
+  }
+}
+
+// out[i] = sum over s < n_sel of w[s] y[s y_stride + i], one fma per term in
+// s order (a fixed order: the same bits whichever grid computes it).
+__global__ void combine_kernel(const float *y, int64_t y_stride, int n_sel, const float *w, int64_t n,
+                               float *out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float acc = 0.0f;
+    for (int s = 0; s < n_sel; ++s) acc = fmaf(w[s], y[s * y_stride + i], acc);
+    out[i] = acc;
   }
 }
 
@@ -1039,9 +1051,11 @@ int qgemv_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win, i
   return launch_gemv(fmt, k, win, n_win, block_rows, stream);
 }
 
-int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert, const int32_t *ids,
-                         int32_t n_sel, const float *x, int64_t x_stride, float *y, int64_t block_rows,
-                         qg_stream_t stream) {
+// The windows of the selected experts, with optional fused transforms: window
+// (m, s) reads x + s x_stride (and x2 + s x_stride for QG_IN_SILU_MUL).
+int expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert, const int32_t *ids, int32_t n_sel,
+                   const float *x, int64_t x_stride, const float *x2, int32_t in_op, float eps, int32_t out_op,
+                   float *y, int64_t block_rows, hipStream_t stream) {
   if (!mats || (n_sel > 0 && !ids)) return QG_E_NULL;
   if (n_mat < 1 || n_sel < 0 || (int64_t)n_mat * n_sel > kMaxWindows || x_stride < 0 || block_rows < 0)
     return QG_E_ARG;
@@ -1056,9 +1070,14 @@ int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert,
   const int64_t out = mats[0].n_rows / n_expert;
   for (int s = 0; s < n_sel; ++s)
     if (ids[s] < 0 || ids[s] >= n_expert) return QG_E_RANGE;
+  if (in_op != QG_IN_X && in_op != QG_IN_RMS && in_op != QG_IN_SILU_MUL) return QG_E_ARG;
+  if (out_op != QG_OUT_Y && out_op != QG_OUT_GELU) return QG_E_ARG;
+  if (in_op == QG_IN_SILU_MUL && out_op == QG_OUT_GELU) return QG_E_ARG;
+  if (in_op == QG_IN_RMS && (!(eps >= 0.0f) || eps > 3.0e38f || mats[0].k > kMaxRmsK)) return QG_E_ARG;
   if (n_sel == 0 || out == 0) return QG_OK;
-  if (!x || !y) return QG_E_NULL;
+  if (!x || !y || (in_op == QG_IN_SILU_MUL && !x2)) return QG_E_NULL;
   qg_window win[kMaxWindows];
+  const float *wx2[kMaxWindows];
   int n = 0;
   for (int m = 0; m < n_mat; ++m)
     for (int s = 0; s < n_sel; ++s) {
@@ -1068,9 +1087,35 @@ int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert,
       win[n].row_end = (int64_t)(ids[s] + 1) * out;
       win[n].x = x + (int64_t)s * x_stride;
       win[n].y = y + ((int64_t)m * n_sel + s) * out;
+      wx2[n] = x2 ? x2 + (int64_t)s * x_stride : nullptr;
       ++n;
     }
-  return launch_gemv(mats[0].fmt, mats[0].k, win, n, block_rows, stream);
+  return launch_gemv(mats[0].fmt, mats[0].k, win, n, block_rows, stream, in_op, eps, out_op, wx2);
+}
+
+int qgemv_expert_windows(const qg_matrix *mats, int32_t n_mat, int64_t n_expert, const int32_t *ids,
+                         int32_t n_sel, const float *x, int64_t x_stride, float *y, int64_t block_rows,
+                         qg_stream_t stream) {
+  return expert_windows(mats, n_mat, n_expert, ids, n_sel, x, x_stride, nullptr, QG_IN_X, 0.0f, QG_OUT_Y, y,
+                        block_rows, stream);
+}
+
+int qgemv_expert_windows_op(const qg_matrix *mats, int32_t n_mat, int64_t n_expert, const int32_t *ids,
+                            int32_t n_sel, const float *x, const float *x2, int64_t x_stride, int32_t in_op,
+                            float eps, int32_t out_op, float *y, int64_t block_rows, qg_stream_t stream) {
+  return expert_windows(mats, n_mat, n_expert, ids, n_sel, x, x_stride, x2, in_op, eps, out_op, y, block_rows,
+                        stream);
+}
+
+int qgemv_combine(const float *y, int64_t y_stride, int32_t n_sel, const float *w, int64_t n, float *out,
+                  qg_stream_t stream) {
+  if (n < 0 || n_sel < 0 || (n_sel > 1 && y_stride < n)) return QG_E_ARG;
+  if (n == 0) return QG_OK;
+  if (!out || (n_sel > 0 && (!y || !w))) return QG_E_NULL;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, y_stride, n_sel, w, n, out);
+  QG_HIP(hipGetLastError());
+  return QG_OK;
 }
 
 int qgemv_silu_mul(const float *g, const float *u, float *h, int64_t n, qg_stream_t stream) {

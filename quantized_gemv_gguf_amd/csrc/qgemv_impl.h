@@ -306,8 +306,16 @@ __device__ __forceinline__ float wave_sum63(float v) {
 // below 0 (which an RMS normalisation of small GELU values would magnify).
 __device__ __forceinline__ float gelu_erf(float t) { return 0.5f * t * erfcf(-t * 0.70710678118654752f); }
 
-// silu(g) * u, as qgemv_silu_mul computes it.
-__device__ __forceinline__ float silu_times(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g) * u = g u / (1 + exp(-g)), with the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each; rounding -g log2(e) adds about
+// |g| 2^-24 relative), so about (|g| + 4) 2^-24 relative in all.  The fused
+// x-load evaluates it for every input a team loads, where a libm exp and an
+// IEEE division (some thirty instructions) doubled a small MoE down grid.
+// qgemv_silu_mul uses this same function, so the two give the same bits.
+__device__ __forceinline__ float silu_times(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
 
 // One wave's partial sums for one staged row and NT tokens: lane l dots
 // blocks l + 64c (c < C) of the wave's slice, staged at byte `ph` of `sb`,

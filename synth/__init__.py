@@ -146,6 +146,14 @@ def expert_ids(n_expert: int, n_sel: int, n_tokens: int, seed: int) -> np.ndarra
     return ids.astype(np.int32)
 
 
+def router_weights(n_tokens: int, n_sel: int, seed: int) -> np.ndarray:
+    """(n_tokens, n_sel) float32 mixing weights of the selected experts: per
+    token, uniform draws in [0.05, 1) scaled to sum to 1."""
+    g = rng(seed)
+    u = g.uniform(0.05, 1.0, size=(n_tokens, n_sel))
+    return (u / u.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 # --- the workloads ----------------------------------------------------------------
 
 def seed_of(cfg: int, tensor_id: int) -> int:

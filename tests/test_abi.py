@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -221,6 +221,31 @@ def test_rows_batch_validation():
     assert call(r0=3, r1=3, x=0, y=0) == 0
     # one token needs no y stride
     assert call(nt=1, ys=0, x=0) == E_NULL
+
+
+def test_expert_windows_op_and_combine_validation():
+    L = q.lib()
+    ids = (ctypes.c_int32 * 2)(1, 3)
+    mats = (q.qg_matrix * 1)(mat(rows=8 * 4, k=64))
+
+    def call(in_op=0, eps=0.0, out_op=0, x=FAKE, x2=FAKE, n_sel=2, m=mats):
+        return L.qgemv_expert_windows_op(m, 1, 4, ids, n_sel, x, x2, 64, in_op, eps, out_op, FAKE, 0, None)
+
+    assert call(in_op=2) == E_ARG and call(in_op=4) == E_ARG and call(out_op=2) == E_ARG
+    assert call(in_op=3, out_op=1) == E_ARG
+    assert call(in_op=1, eps=-1.0) == E_ARG
+    assert call(in_op=3, x2=0) == E_NULL
+    assert call(x=0) == E_NULL
+    assert call(n_sel=0, x=0, x2=0) == 0
+    big = (q.qg_matrix * 1)(mat(rows=4, k=32768 + 32))
+    assert call(in_op=1, m=big) == E_ARG  # the fused RMS takes k <= 32768
+    assert L.qgemv_combine(FAKE, 8, 2, FAKE, -1, FAKE, None) == E_ARG
+    assert L.qgemv_combine(FAKE, 7, 2, FAKE, 8, FAKE, None) == E_ARG  # expert outputs would overlap
+    assert L.qgemv_combine(FAKE, 8, -1, FAKE, 8, FAKE, None) == E_ARG
+    assert L.qgemv_combine(0, 8, 2, FAKE, 8, FAKE, None) == E_NULL
+    assert L.qgemv_combine(FAKE, 8, 2, 0, 8, FAKE, None) == E_NULL
+    assert L.qgemv_combine(FAKE, 8, 2, FAKE, 8, 0, None) == E_NULL
+    assert L.qgemv_combine(0, 0, 0, 0, 0, 0, None) == 0
 
 
 def test_rows_op_validation():

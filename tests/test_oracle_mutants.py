@@ -62,6 +62,8 @@ MUTANTS = [
      "double d = orc_half_to_double((uint16_t)(b[0] | (b[1] << 8)));"),
     ("q6k_unsigned_scale", "const int8_t *scale = (const int8_t *)(b + 192);", "const uint8_t *scale = b + 192;"),
     ("kquant_block_weights_32", "return (fmt == ORC_Q4_K || fmt == ORC_Q6_K) ? 256 : 32;", "return 32;"),
+    ("combine_stride_dropped", "acc += w[s] * y[s * y_stride + i];", "acc += w[s] * y[i];"),
+    ("combine_weight_index", "acc += w[s] * y[s * y_stride + i];", "acc += w[0] * y[s * y_stride + i];"),
 ]
 
 # pins, cheapest first; a mutant is caught at the first one that fails
@@ -87,6 +89,7 @@ PINS = [
     pins.test_q6_k_codes_are_a_bijection_and_centered,
     pins.test_q6_k_scales_cover_runs_of_16,
     pins.test_q6_k_hand_built_blocks,
+    pins.test_combine_against_exact_rationals_and_special_cases,
 ]
 
 PARAMS = {

@@ -605,3 +605,25 @@ def test_kquant_layout_is_row_major_out_by_in():
             x[i] = 1.0
             y, _ = oracle.gemv_rows(fmt, w, rows, k, x)
             assert np.array_equal(y, dec[:, i].astype(np.float64))
+
+
+# --- router-weighted combine -------------------------------------------------------------
+
+def test_combine_against_exact_rationals_and_special_cases():
+    g = np.random.default_rng(8)
+    y = g.standard_normal((4, 33))
+    w = g.uniform(0.05, 1.0, 4)
+    got = oracle.combine(y, w)
+    for i in range(33):
+        exact = sum(Fraction(float(w[s])) * Fraction(float(y[s, i])) for s in range(4))
+        absum = sum(abs(Fraction(float(w[s])) * Fraction(float(y[s, i]))) for s in range(4))
+        assert abs(Fraction(got[i]) - exact) <= 4 * Fraction(2) ** -53 * absum
+    # one-hot weights select one expert's vector exactly; zero weights give zeros
+    for s in range(4):
+        e = np.zeros(4)
+        e[s] = 1.0
+        assert np.array_equal(oracle.combine(y, e), y[s])
+    assert np.array_equal(oracle.combine(y, np.zeros(4)), np.zeros(33))
+    assert np.array_equal(oracle.combine(np.zeros((0, 5)), np.zeros(0)), np.zeros(5))
+    # the product w^T Y, as numpy's matrix product computes it
+    assert np.allclose(got, w @ y, rtol=1e-14, atol=1e-14)
