@@ -622,11 +622,12 @@ def q4_0_workload(args, dev):
 def moe_workload(args, dev):
     """MXFP4 MoE expert GEMV: stacked (128, 2880, 2880) gate/up/down, 4 of 128
     experts per token (seeded uniform top-4), 64 tokens.  Per token: one grid
-    over the 8 gate/up windows of the selected experts, SiLU*up, one grid over
-    the 4 down windows, and the router-weighted combine of the 4 expert
-    outputs (seeded weights).  (SiLU*up fused into the down grid's x-load,
-    qgemv_expert_windows_op, is slower here: every one of the ~1,400 teams
-    of that small grid evaluates it for its whole input slice.)"""
+    over the selected experts' gate and up rows in pairs, storing
+    silu(gate) * up (qgemv_expert_swiglu), one grid over the 4 down windows,
+    and the router-weighted combine of the 4 expert outputs (seeded weights).
+    (SiLU*up fused into the down grid's x-load instead, qgemv_expert_windows_op,
+    is slower here: every one of the ~1,400 teams of that small grid evaluates
+    it for its whole input slice.)"""
     import torch
     import quantized_gemv_gguf_amd as q
     c = synth.CONFIGS[4]
@@ -645,13 +646,15 @@ def moe_workload(args, dev):
     st = torch.cuda.current_stream().cuda_stream
     m2 = (q.qg_matrix * 2)(mats[0].c(), mats[1].c())
     m1 = (q.qg_matrix * 1)(mats[2].c())
+    gate_c, up_c = mats[0].c(), mats[1].c()
+    gate_m, up_m = ctypes.byref(gate_c), ctypes.byref(up_c)
     idarr = [(ctypes.c_int32 * ns)(*[int(v) for v in ids[t]]) for t in range(c["tokens"])]
     B = args.block_rows
 
     def token(t):
         t = t % c["tokens"]
-        rc = L.qgemv_expert_windows(m2, 2, E, idarr[t], ns, xs[t].data_ptr(), 0, gu.data_ptr(), B, st)
-        rc |= L.qgemv_silu_mul(gu.data_ptr(), gu.data_ptr() + 4 * ns * out, h.data_ptr(), ns * out, st)
+        rc = L.qgemv_expert_swiglu(gate_m, up_m, E, idarr[t], ns, xs[t].data_ptr(), 0, q.IN_X, 0.0, h.data_ptr(),
+                                   B, st)
         rc |= L.qgemv_expert_windows(m1, 1, E, idarr[t], ns, h.data_ptr(), out, ye.data_ptr(), B, st)
         rc |= L.qgemv_combine(ye.data_ptr(), out, ns, wts[t].data_ptr(), out, y[t].data_ptr(), st)
         assert rc == 0
@@ -666,7 +669,7 @@ def moe_workload(args, dev):
             "bytes_per_token": per_tok,
             "config": {"workload": c["name"], "format": "MXFP4", "n_expert": E, "out": out, "k": k,
                        "experts_per_token": ns, "tokens": n, "block_rows": B,
-                       "launches_per_token": "gate/up grid, SiLU*up, down grid, combine",
+                       "launches_per_token": "gate/up pair grid storing SiLU*up, down grid, combine",
                        "resident_bytes": 3 * q.qgemv_weight_bytes(q.MXFP4, rows, k)}}
 
 

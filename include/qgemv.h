@@ -237,6 +237,28 @@ int qgemv_expert_windows_op(const qg_matrix *mats, int32_t n_mat, int64_t n_expe
                             const float *x2, int64_t x_stride, int32_t in_op, float eps,
                             int32_t out_op, float *y, int64_t block_rows, qg_stream_t stream);
 
+/* SwiGLU gate and up projections in one grid: h[j] = silu(gate_j . x') *
+ * (up_j . x') for rows j in [row_start, row_end), x' = x or rms(x) (in_op
+ * QG_IN_X or QG_IN_RMS, eps and k <= 32768 as qgemv_rows_op).  Each team
+ * computes a gate row and the up row of the same index back to back and
+ * stores only their SwiGLU product (neurostream README, "How it works": the
+ * two-phase FFN whose first phase is gate and up; hipfire PR, "Design
+ * notes": the fused weight_gemv_swiglu step), so neither projection is
+ * written out and no elementwise launch follows.  gate and up must match in
+ * fmt, k and n_rows (else QG_E_SHAPE); h is device, row_end - row_start
+ * floats.  Bits equal qgemv_rows (or _op) of each, then qgemv_silu_mul. */
+int qgemv_rows_swiglu(const qg_matrix *gate, const qg_matrix *up, int64_t row_start,
+                      int64_t row_end, const float *x, int32_t in_op, float eps, float *h,
+                      int64_t block_rows, qg_stream_t stream);
+
+/* The same for selected experts of stacked (n_expert, out, k) gate and up
+ * tensors (as qgemv_expert_windows): expert s reads x + s * x_stride and
+ * writes h + s * out; all n_sel <= QG_MAX_WINDOWS experts in one grid. */
+int qgemv_expert_swiglu(const qg_matrix *gate, const qg_matrix *up, int64_t n_expert,
+                        const int32_t *ids, int32_t n_sel, const float *x, int64_t x_stride,
+                        int32_t in_op, float eps, float *h, int64_t block_rows,
+                        qg_stream_t stream);
+
 /* Router-weighted combine of the selected experts' outputs: out[i] =
  * sum_{s < n_sel} w[s] * y[s * y_stride + i], one fp32 fma per term in s
  * order (neurostream README, "How it works": the router names the active

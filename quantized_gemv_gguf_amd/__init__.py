@@ -86,6 +86,10 @@ def lib():
         "qgemv_expert_windows_op": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _vp, _i64, _i32, ctypes.c_float,
                                      _i32, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_combine": ([_vp, _i64, _i32, _vp, _i64, _vp, _vp], ctypes.c_int),
+        "qgemv_rows_swiglu": ([P(qg_matrix), P(qg_matrix), _i64, _i64, _vp, _i32, ctypes.c_float, _vp, _i64, _vp],
+                              ctypes.c_int),
+        "qgemv_expert_swiglu": ([P(qg_matrix), P(qg_matrix), _i64, P(_i32), _i32, _vp, _i64, _i32, ctypes.c_float,
+                                 _vp, _i64, _vp], ctypes.c_int),
         "qgemv_rows_op": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _i64, _vp],
                           ctypes.c_int),
         "qgemv_expert_windows": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _i64, _vp, _i64, _vp],
@@ -279,6 +283,28 @@ def qgemv_expert_windows_op(mats: Sequence[Matrix], n_expert: int, ids, x, x_str
     _check(lib().qgemv_expert_windows_op(marr, len(mats), n_expert, iarr, len(ids), xp, x2p, x_stride, int(in_op),
                                          float(eps), int(out_op), yp, block_rows, _stream(stream)),
            "qgemv_expert_windows_op")
+
+
+def qgemv_rows_swiglu(gate: Matrix, up: Matrix, row_start: int, row_end: int, x, h, in_op: int = 0,
+                      eps: float = 0.0, block_rows: int = 0, stream=None) -> None:
+    """h = silu(gate[rows] . x') * (up[rows] . x'), x' = x (IN_X) or rms(x) (IN_RMS)."""
+    g, u = gate.c(), up.c()
+    n = max(row_end - row_start, 0)
+    _check(lib().qgemv_rows_swiglu(ctypes.byref(g), ctypes.byref(u), row_start, row_end, _f32(x, gate.k, "x"),
+                                   int(in_op), float(eps), _f32(h, n, "h"), block_rows, _stream(stream)),
+           "qgemv_rows_swiglu")
+
+
+def qgemv_expert_swiglu(gate: Matrix, up: Matrix, n_expert: int, ids, x, x_stride: int, h, in_op: int = 0,
+                        eps: float = 0.0, block_rows: int = 0, stream=None) -> None:
+    ids = [int(i) for i in ids]
+    g, u = gate.c(), up.c()
+    iarr = (_i32 * max(len(ids), 1))(*ids)
+    out = gate.n_rows // n_expert if n_expert > 0 else 0
+    xp = _f32(x, gate.k + (len(ids) - 1) * x_stride if ids else 0, "x")
+    _check(lib().qgemv_expert_swiglu(ctypes.byref(g), ctypes.byref(u), n_expert, iarr, len(ids), xp, x_stride,
+                                     int(in_op), float(eps), _f32(h, len(ids) * out, "h"), block_rows,
+                                     _stream(stream)), "qgemv_expert_swiglu")
 
 
 def qgemv_combine(y, y_stride: int, n_sel: int, w, n: int, out, stream=None) -> None:

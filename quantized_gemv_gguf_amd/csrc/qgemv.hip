@@ -57,6 +57,8 @@ extern template GemvFn pick_op<kOpRms>(int32_t, Shape);
 extern template GemvFn pick_op<kOpRmsGelu>(int32_t, Shape);
 extern template GemvFn pick_op<kOpSilu>(int32_t, Shape);
 extern template GemvFn pick_op<kOpGelu>(int32_t, Shape);
+extern template GemvFn pick_op<kOpSwiglu>(int32_t, Shape);
+extern template GemvFn pick_op<kOpRmsSwiglu>(int32_t, Shape);
 extern template GemvFn pick_batch<2>(int32_t, Shape);
 extern template GemvFn pick_batch<4>(int32_t, Shape);
 }  // namespace qgemv_detail
@@ -857,29 +859,40 @@ GemvFn pick(int32_t fmt, Shape s, int32_t in_op, int32_t out_op) {
 // in_op / out_op / eps: the fused transforms (QG_IN_X, QG_OUT_Y: none); x2[i]
 // is window i's SiLU multiplier (x2 may be null when in_op is not
 // QG_IN_SILU_MUL).  nt > 1: nt tokens (2 or 4, no transform), token t's x at
-// win.x + t x_stride and its y at win.y + t y_stride.
+// win.x + t x_stride and its y at win.y + t y_stride.  up: SwiGLU pairs,
+// up[i] the row 0 of window i's up matrix (win.data the gate's; same shape),
+// y[j] = silu(gate_j . x) * (up_j . x); the kernel walks virtual rows, two
+// per output row.
 int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
                 hipStream_t stream, int32_t in_op = QG_IN_X, float eps = 0.0f, int32_t out_op = QG_OUT_Y,
-                const float *const *x2 = nullptr, int nt = 1, int64_t x_stride = 0, int64_t y_stride = 0) {
+                const float *const *x2 = nullptr, int nt = 1, int64_t x_stride = 0, int64_t y_stride = 0,
+                const void *const *up = nullptr) {
   Shape s;
   int rc = team_shape(fmt, k, &s);
   if (rc) return rc;
+  const int64_t pm = up ? 2 : 1;  // virtual rows per output row
   qg_window win[kMaxWindows];
   const float *wx2[kMaxWindows];
+  const void *wup[kMaxWindows];
   int n = 0;
   int64_t maxlen = 1, total = 0;
   for (int i = 0; i < n_in; ++i) {
     if (win_in[i].row_end == win_in[i].row_start) continue;
     wx2[n] = x2 ? x2[i] : nullptr;
-    win[n++] = win_in[i];
-    maxlen = std::max<int64_t>(maxlen, win_in[i].row_end - win_in[i].row_start);
-    total += win_in[i].row_end - win_in[i].row_start;
+    wup[n] = up ? up[i] : nullptr;
+    win[n] = win_in[i];
+    win[n].row_start *= pm;
+    win[n].row_end *= pm;
+    maxlen = std::max<int64_t>(maxlen, win[n].row_end - win[n].row_start);
+    total += win[n].row_end - win[n].row_start;
+    ++n;
   }
   if (n == 0) return QG_OK;
-  const int64_t B = block_rows > 0 ? std::min<int64_t>(block_rows, maxlen) : maxlen;
+  const int64_t B = block_rows > 0 ? std::min<int64_t>(pm * block_rows, maxlen) : maxlen;
   const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * gemv_teams_per_cu(fmt, s.wt));
-  const int tile_rows =
+  int tile_rows =
       (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kGemvTileRows, B, (total + teams_max - 1) / teams_max}));
+  if (up) tile_rows = std::max(2, tile_rows & ~1);  // whole pairs (B and every window are even)
   GemvArgs a;
   memset(&a, 0, sizeof(a));
   int64_t tiles = 0;
@@ -888,6 +901,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
     const int64_t len = win[i].row_end - win[i].row_start;
     const int64_t full = len / B, rem = len - full * B;
     a.win[i].base = (const uint8_t *)win[i].data;
+    a.win[i].base2 = (const uint8_t *)wup[i];
     a.win[i].x = win[i].x;
     a.win[i].x2 = wx2[i];
     a.win[i].y = win[i].y;
@@ -911,7 +925,10 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   a.x_stride = x_stride;
   a.y_stride = y_stride;
   const int64_t teams = std::min<int64_t>(teams_max, tiles);
-  const GemvFn fn = nt == 1 ? pick(fmt, s, in_op, out_op)
+  const GemvFn fn = up ? (in_op == QG_IN_RMS ? pick_op<kOpRmsSwiglu>(fmt, s)
+                          : in_op == QG_IN_X  ? pick_op<kOpSwiglu>(fmt, s)
+                                              : nullptr)
+                    : nt == 1 ? pick(fmt, s, in_op, out_op)
                     : nt == 2 && in_op == QG_IN_X && out_op == QG_OUT_Y ? pick_batch<2>(fmt, s)
                     : nt == 4 && in_op == QG_IN_X && out_op == QG_OUT_Y ? pick_batch<4>(fmt, s)
                                                                         : nullptr;
@@ -1105,6 +1122,57 @@ int qgemv_expert_windows_op(const qg_matrix *mats, int32_t n_mat, int64_t n_expe
                             float eps, int32_t out_op, float *y, int64_t block_rows, qg_stream_t stream) {
   return expert_windows(mats, n_mat, n_expert, ids, n_sel, x, x_stride, x2, in_op, eps, out_op, y, block_rows,
                         stream);
+}
+
+namespace {
+// Checks shared by the SwiGLU-pair entry points: gate and up are twins.
+int check_pair(const qg_matrix *gate, const qg_matrix *up, int32_t in_op, float eps) {
+  int rc = check_matrix(gate);
+  if (rc) return rc;
+  if ((rc = check_matrix(up))) return rc;
+  if (up->fmt != gate->fmt || up->k != gate->k || up->n_rows != gate->n_rows) return QG_E_SHAPE;
+  if (in_op != QG_IN_X && in_op != QG_IN_RMS) return QG_E_ARG;
+  if (in_op == QG_IN_RMS && (!(eps >= 0.0f) || eps > 3.0e38f || gate->k > kMaxRmsK)) return QG_E_ARG;
+  return QG_OK;
+}
+}  // namespace
+
+int qgemv_rows_swiglu(const qg_matrix *gate, const qg_matrix *up, int64_t row_start, int64_t row_end,
+                      const float *x, int32_t in_op, float eps, float *h, int64_t block_rows, qg_stream_t stream) {
+  if (!gate || !up) return QG_E_NULL;
+  int rc = check_pair(gate, up, in_op, eps);
+  if (rc) return rc;
+  if ((rc = check_range(gate->n_rows, row_start, row_end))) return rc;
+  if (block_rows < 0) return QG_E_ARG;
+  if (row_end == row_start) return QG_OK;
+  if (!x || !h) return QG_E_NULL;
+  qg_window win = {gate->data, gate->n_rows, row_start, row_end, x, h};
+  const void *upd = up->data;
+  return launch_gemv(gate->fmt, gate->k, &win, 1, block_rows, stream, in_op, eps, QG_OUT_Y, nullptr, 1, 0, 0, &upd);
+}
+
+int qgemv_expert_swiglu(const qg_matrix *gate, const qg_matrix *up, int64_t n_expert, const int32_t *ids,
+                        int32_t n_sel, const float *x, int64_t x_stride, int32_t in_op, float eps, float *h,
+                        int64_t block_rows, qg_stream_t stream) {
+  if (!gate || !up || (n_sel > 0 && !ids)) return QG_E_NULL;
+  int rc = check_pair(gate, up, in_op, eps);
+  if (rc) return rc;
+  if (n_sel < 0 || n_sel > kMaxWindows || x_stride < 0 || block_rows < 0) return QG_E_ARG;
+  if (n_expert <= 0 || gate->n_rows % n_expert != 0) return QG_E_SHAPE;
+  const int64_t out = gate->n_rows / n_expert;
+  for (int s = 0; s < n_sel; ++s)
+    if (ids[s] < 0 || ids[s] >= n_expert) return QG_E_RANGE;
+  if (n_sel == 0 || out == 0) return QG_OK;
+  if (!x || !h) return QG_E_NULL;
+  qg_window win[kMaxWindows];
+  const void *upd[kMaxWindows];
+  for (int s = 0; s < n_sel; ++s) {
+    win[s] = {gate->data, gate->n_rows, (int64_t)ids[s] * out, (int64_t)(ids[s] + 1) * out,
+              x + (int64_t)s * x_stride, h + (int64_t)s * out};
+    upd[s] = up->data;
+  }
+  return launch_gemv(gate->fmt, gate->k, win, n_sel, block_rows, stream, in_op, eps, QG_OUT_Y, nullptr, 1, 0, 0,
+                     upd);
 }
 
 int qgemv_combine(const float *y, int64_t y_stride, int32_t n_sel, const float *w, int64_t n, float *out,

@@ -262,6 +262,7 @@ template <> struct Fmt<QG_Q6_K> {
 
 struct WinDev {
   const uint8_t *base;  // row 0 of the window's matrix (16-byte aligned)
+  const uint8_t *base2; // SwiGLU pairs: row 0 of the up matrix (base is the gate's)
   const float *x;
   const float *x2;      // the multiplier of QG_IN_SILU_MUL, else unused
   float *y;             // y[r - row_start] <-> row r
@@ -439,11 +440,17 @@ __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmc
 // The fused transforms a launch applies, fixed at compile time: code for an
 // op a launch does not use (even behind a runtime branch) made the plain GEMV
 // up to 17% slower.
-enum GemvOp { kOpNone = 0, kOpRms = 1, kOpRmsGelu = 2, kOpSilu = 3, kOpGelu = 4 };
+// kOpSwiglu / kOpRmsSwiglu: the window pairs a gate and an up matrix; its
+// "rows" alternate gate row r, up row r (virtual row 2r, 2r + 1), and the
+// store writes silu(gate . x) * (up . x) once per pair.
+enum GemvOp { kOpNone = 0, kOpRms = 1, kOpRmsGelu = 2, kOpSilu = 3, kOpGelu = 4, kOpSwiglu = 5, kOpRmsSwiglu = 6 };
 __host__ __device__ constexpr int op_in(int op) {
-  return op == kOpRms || op == kOpRmsGelu ? QG_IN_RMS : op == kOpSilu ? QG_IN_SILU_MUL : QG_IN_X;
+  return op == kOpRms || op == kOpRmsGelu || op == kOpRmsSwiglu ? QG_IN_RMS
+         : op == kOpSilu                                        ? QG_IN_SILU_MUL
+                                                                : QG_IN_X;
 }
 __host__ __device__ constexpr bool op_gelu(int op) { return op == kOpRmsGelu || op == kOpGelu; }
+__host__ __device__ constexpr bool op_pair(int op) { return op == kOpSwiglu || op == kOpRmsSwiglu; }
 
 // NT > 1: NT tokens per launch (a small batch): every block is staged and
 // decoded once and dotted with each token's activations, in the one-token
@@ -451,6 +458,7 @@ __host__ __device__ constexpr bool op_gelu(int op) { return op == kOpRmsGelu || 
 template <int FMT, int WT, int C, int OP, int NT = 1>
 __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   static_assert(NT == 1 || OP == kOpNone, "fused transforms take one token");
+  static_assert(!op_pair(OP) || kGemvTileRows % 2 == 0, "SwiGLU tiles hold whole pairs");
   using G = Geo<FMT, C>;
   constexpr int V = G::V, SLOT = G::SLOT;
   constexpr int NB = gemv_in_flight(FMT, WT), NS = NB + 1;
@@ -479,10 +487,12 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   const int TR = a.tile_rows;
   const int tpb = a.tiles_per_block;
   const float eps = a.eps;
+  constexpr bool kPair = op_pair(OP);
   struct Win {
     int w, t0, t1;  // window index, its tiles [t0, t1)
-    int64_t row_start, row_end;
+    int64_t row_start, row_end;  // (SwiGLU pairs: virtual rows, two per output)
     const uint8_t *base;  // row 0, advanced to the wave's slice
+    const uint8_t *base2; // SwiGLU pairs: the up matrix's, likewise
     const float *x, *x2;
     float *y;
   };
@@ -493,9 +503,15 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     W.row_start = a.win[w].row_start;
     W.row_end = a.win[w].row_end;
     W.base = a.win[w].base + slice_off;
+    if constexpr (kPair) W.base2 = a.win[w].base2 + slice_off;
     W.x = a.win[w].x;
     W.x2 = a.win[w].x2;
     W.y = a.win[w].y;
+  };
+  // The wave's slice of (virtual) row v of window W.
+  auto row_ptr = [&](const Win &W, int64_t v) -> const uint8_t * {
+    if constexpr (kPair) return ((v & 1) ? W.base2 : W.base) + (v >> 1) * rb;
+    return W.base + v * rb;
   };
   struct Tile {
     int t, nrows;
@@ -630,18 +646,24 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   locate(blockIdx.x, CW, cur);
   FW = CW;
   F = cur;
-  const uint8_t *fp = FW.base + F.r0 * rb;
+  const uint8_t *fp = row_ptr(FW, F.r0);
+  int64_t f_v = F.r0;  // SwiGLU pairs: the virtual row fp points at
   int f_left = F.nrows;
   bool f_end = false;
   auto advance_fetch = [&]() {
     if (f_end) return;
     if (--f_left > 0) {
-      fp += rb;
+      if constexpr (kPair) {
+        fp = row_ptr(FW, ++f_v);
+      } else {
+        fp += rb;
+      }
       return;
     }
     if (F.t + T < n_tiles) {
       locate(F.t + T, FW, F);
-      fp = FW.base + F.r0 * rb;
+      fp = row_ptr(FW, F.r0);
+      f_v = F.r0;
       f_left = F.nrows;
     } else {
       f_end = true;
@@ -680,7 +702,12 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
         advance_fetch();
         wait_vmcnt<V * NB>();  // this row's copies have landed
         const uint8_t *sb = &ring[wave][slot][0];
-        const int ph = (int)((ph0 + (uint32_t)i * rb16) & 15);
+        int ph;
+        if constexpr (kPair) {
+          ph = (int)((uintptr_t)row_ptr(CW, cur.r0 + i) & 15);
+        } else {
+          ph = (int)((ph0 + (uint32_t)i * rb16) & 15);
+        }
         float part[NT];
         row_partial<FMT, C, NT>(sb, ph, lane, slice_n, xr, xs, part);
 #pragma unroll
@@ -688,8 +715,40 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
         slot = slot + 1 == NS ? 0 : slot + 1;
       }
     }
-    float *yt = CW.y + (cur.r0 - CW.row_start);
     constexpr bool gelu_out = op_gelu(OP);
+    if constexpr (kPair) {
+      // tiles start at even virtual rows and hold whole pairs
+      float *yt = CW.y + ((cur.r0 - CW.row_start) >> 1);
+      const int npair = nrows >> 1;
+      if (WT == 1) {
+        if (lane == 63) {
+#pragma unroll
+          for (int j = 0; j < kGemvTileRows / 2; ++j)
+            if (j < npair) yt[j] = silu_times(acc[0][2 * j], acc[0][2 * j + 1]);
+        }
+      } else {
+        if (lane == 63) {
+#pragma unroll
+          for (int i = 0; i < kGemvTileRows; ++i) red[parity][wave][i] = acc[0][i];
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < npair) {
+          const int j = threadIdx.x;
+          float g = red[parity][0][2 * j], u = red[parity][0][2 * j + 1];
+#pragma unroll
+          for (int v = 1; v < WT; ++v) {
+            g += red[parity][v][2 * j];
+            u += red[parity][v][2 * j + 1];
+          }
+          yt[j] = silu_times(g, u);
+        }
+        parity ^= 1;
+      }
+      if (cur.t + T >= n_tiles) break;
+      locate(cur.t + T, CW, cur);
+      continue;
+    }
+    float *yt = CW.y + (cur.r0 - CW.row_start);
     if (WT == 1) {
       if (lane == 63) {
 #pragma unroll

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 28, names
+    assert len(names) == 30, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -246,6 +246,39 @@ def test_expert_windows_op_and_combine_validation():
     assert L.qgemv_combine(FAKE, 8, 2, 0, 8, FAKE, None) == E_NULL
     assert L.qgemv_combine(FAKE, 8, 2, FAKE, 8, 0, None) == E_NULL
     assert L.qgemv_combine(0, 0, 0, 0, 0, 0, None) == 0
+
+
+def test_swiglu_validation():
+    L = q.lib()
+    g, u = mat(rows=8, k=64), mat(rows=8, k=64)
+
+    def rows(gm=None, um=None, r0=0, r1=8, x=FAKE, op=0, eps=0.0, h=FAKE, B=0):
+        gm = g if gm is None else gm
+        um = u if um is None else um
+        return L.qgemv_rows_swiglu(ctypes.byref(gm), ctypes.byref(um), r0, r1, x, op, eps, h, B, None)
+
+    assert L.qgemv_rows_swiglu(None, ctypes.byref(u), 0, 8, FAKE, 0, 0.0, FAKE, 0, None) == E_NULL
+    assert rows(um=mat(rows=9, k=64)) == E_SHAPE
+    assert rows(um=mat(fmt=2, rows=8, k=64)) == E_SHAPE
+    assert rows(um=mat(rows=8, k=96)) == E_SHAPE
+    assert rows(op=3) == E_ARG and rows(op=2) == E_ARG
+    assert rows(op=1, eps=-1.0) == E_ARG
+    assert rows(r1=9) == E_RANGE
+    assert rows(B=-1) == E_ARG
+    assert rows(x=0) == E_NULL and rows(h=0) == E_NULL
+    assert rows(r0=4, r1=4, x=0, h=0) == 0
+    ids = (ctypes.c_int32 * 2)(0, 3)
+    eg, eu = mat(rows=16, k=64), mat(rows=16, k=64)
+
+    def exp(n_expert=4, n_sel=2, x=FAKE, xs=64, op=0, h=FAKE, idp=ids):
+        return L.qgemv_expert_swiglu(ctypes.byref(eg), ctypes.byref(eu), n_expert, idp, n_sel, x, xs, op, 0.0, h, 0,
+                                     None)
+
+    assert exp(n_expert=0) == E_SHAPE and exp(n_expert=3) == E_SHAPE
+    assert exp(n_expert=2) == E_RANGE  # id 3 >= 2
+    assert exp(n_sel=-1) == E_ARG and exp(n_sel=65) == E_ARG and exp(xs=-1) == E_ARG
+    assert exp(idp=None) == E_NULL and exp(x=0) == E_NULL and exp(h=0) == E_NULL
+    assert exp(n_sel=0, x=0, h=0) == 0
 
 
 def test_rows_op_validation():
