@@ -483,6 +483,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
   // make every load touch 64 cache lines, and when every workgroup reads x at
   // once right after the barrier those requests queue for microseconds.
   float xr[C][32];
+  float xs[C][2] = {};  // unit_sums(xr) for the formats whose dot takes them
   auto gather_x = [&](const float *xg, int b0, int nb, float (&out)[32]) {
     const QG_GLOBAL float *x = (const QG_GLOBAL float *)xg + 32 * min(b0, nb - 1);
     const int nbr = min(64, nb - b0);                  // blocks of the run (<= 0: none)
@@ -542,6 +543,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         xr[c][4 * q + 3] = ok ? v.w : 0.0f;
       }
     }
+    if constexpr (Fmt<FMT>::kSums) unit_sums<C>(xr, xs);
   };
 
   // Wave 0 runs the barrier, whose release steps wait for all of the wave's
@@ -659,6 +661,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         for (int c = 0; c < C; ++c)
 #pragma unroll
           for (int e = 0; e < 32; ++e) xr[c][e] *= inv;
+        if constexpr (Fmt<FMT>::kSums) unit_sums<C>(xr, xs);
       }
       xw = INT32_MAX;
     }
@@ -687,7 +690,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
         if (i < nrows) {
           __builtin_amdgcn_wave_barrier();
           const int ph = (int)((uintptr_t)(done.row0 + (uint32_t)i * done.rb) & 15);
-          const float sp = row_partial<FMT, C>(sb, ph, lane, done.slice_n, xr, kNoSums<C>);
+          const float sp = row_partial<FMT, C>(sb, ph, lane, done.slice_n, xr, xs);
           acc[i] = wave_sum63(sp);
           __builtin_amdgcn_wave_barrier();
         }

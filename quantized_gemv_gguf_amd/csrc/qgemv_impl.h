@@ -41,6 +41,7 @@ template <int FMT> struct Fmt;
 // Q8_0: fp16 d, 32 x int8 q; w = d * q (RAMforge README, "Milestone 5").
 template <> struct Fmt<QG_Q8_0> {
   static constexpr int kBytes = 34, kScaleBytes = 2, kWords = 8, kUnits = 1;
+  static constexpr bool kSums = false, kDot = false;
   struct Scale { float d; };
   __device__ static inline Scale scale(uint32_t bits) {
     return Scale{__half2float(__ushort_as_half((uint16_t)bits))};
@@ -58,11 +59,18 @@ template <> struct Fmt<QG_Q8_0> {
 
 // Q4_0: fp16 d, 16 bytes of nibbles; w = d * (q - 8) (RAMforge README,
 // "Milestone 5").  Element j < 16 is the low nibble of byte j, element j + 16
-// the high nibble.  (q ^ 8) is q - 8 in 4-bit two's complement; moved to the
-// top of a byte it reads as the int8 16 * (q - 8), exactly, and the 1/16 goes
-// into the scale (a power of two, so d/16 is exact too).
+// the high nibble.  Decode (the dequant kernel): (q ^ 8) is q - 8 in 4-bit
+// two's complement; moved to the top of a byte it reads as the int8
+// 16 * (q - 8), exactly, and the 1/16 goes into the scale (a power of two, so
+// d/16 is exact too).  Dot (the GEMV): two codes per word become fp16
+// subnormals q 2^-24 that v_fma_mix_f32 multiplies into the fp32 sums with no
+// conversion instruction (7 bit operations and 8 FMAs per 8 weights, against
+// 3 + 8 conversions + 8 FMAs), and the offset comes out as
+// d (2^24 sum q x - 8 sum x), with sum x per block formed once per
+// activation vector.
 template <> struct Fmt<QG_Q4_0> {
   static constexpr int kBytes = 18, kScaleBytes = 2, kWords = 4, kUnits = 1;
+  static constexpr bool kSums = true, kDot = true;
   struct Scale { float d16; };
   __device__ static inline Scale scale(uint32_t bits) {
     return Scale{__half2float(__ushort_as_half((uint16_t)bits)) * 0.0625f};
@@ -82,6 +90,10 @@ template <> struct Fmt<QG_Q4_0> {
   }
   __device__ static inline float apply(Scale s, float v) { return s.d16 * v; }
   __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d16, v, acc); }
+  // res[t] = acc[t] + the block's dot with token t's inputs.
+  template <int NT>
+  __device__ static inline void dot(const uint8_t *blk, const float (&x)[NT][32], const float (&xs)[NT][2],
+                                    const float (&acc)[NT], float (&res)[NT]);
 };
 
 // MXFP4: E8M0 e, 16 bytes of E2M1 nibbles; w = 2^(e-127) * E2M1(nib) (block
@@ -91,6 +103,7 @@ template <> struct Fmt<QG_Q4_0> {
 // exact ldexp, and e = 255 gives NaN.
 template <> struct Fmt<QG_MXFP4> {
   static constexpr int kBytes = 17, kScaleBytes = 1, kWords = 4, kUnits = 1;
+  static constexpr bool kSums = false, kDot = false;
   struct Scale { int e; };
   __device__ static inline Scale scale(uint32_t bits) { return Scale{(int)(bits & 0xffu)}; }
   // f = (value of the byte's low nibble, value of its high nibble)
@@ -121,6 +134,35 @@ __device__ __forceinline__ float h16_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
+template <int NT>
+__device__ inline void Fmt<QG_Q4_0>::dot(const uint8_t *blk, const float (&x)[NT][32], const float (&xs)[NT][2],
+                                         const float (&acc)[NT], float (&res)[NT]) {
+  uint32_t sbits = 0, q[4];
+  __builtin_memcpy(&sbits, blk, 2);
+  __builtin_memcpy(q, blk + 2, 16);
+  const float d = half_bits(sbits);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // word i: low nibbles are elements 4i..4i+3, high nibbles 16+4i..16+4i+3
+      const uint32_t a = q[i] & 0x000F000Fu, b = (q[i] >> 8) & 0x000F000Fu;
+      const uint32_t c = (q[i] >> 4) & 0x000F000Fu, e = (q[i] >> 12) & 0x000F000Fu;
+      p[0] = fmaf(h16_lo(a), x[t][4 * i + 0], p[0]);
+      p[1] = fmaf(h16_lo(b), x[t][4 * i + 1], p[1]);
+      p[2] = fmaf(h16_hi(a), x[t][4 * i + 2], p[2]);
+      p[3] = fmaf(h16_hi(b), x[t][4 * i + 3], p[3]);
+      p[0] = fmaf(h16_lo(c), x[t][16 + 4 * i + 0], p[0]);
+      p[1] = fmaf(h16_lo(e), x[t][16 + 4 * i + 1], p[1]);
+      p[2] = fmaf(h16_hi(c), x[t][16 + 4 * i + 2], p[2]);
+      p[3] = fmaf(h16_hi(e), x[t][16 + 4 * i + 3], p[3]);
+    }
+    const float r = fmaf(d * 0x1p24f, (p[0] + p[1]) + (p[2] + p[3]), acc[t]);
+    res[t] = fmaf(-8.0f * d, xs[t][0] + xs[t][1], r);
+  }
+}
+
 // Q4_K: 144-byte super-block of 256 weights = fp16 d, fp16 dmin, 12 bytes of
 // packed 6-bit sub-block scales sc and mins m, 128 bytes of nibbles;
 // w = d sc q - dmin m (RAMforge README, "Milestone 5", Q4_K line), in GGUF's
@@ -136,6 +178,7 @@ __device__ __forceinline__ float h16_hi(uint32_t v) {
 // sums are those of the plain codes, bit for bit.
 template <> struct Fmt<QG_Q4_K> {
   static constexpr int kBytes = 144, kUnits = 8;
+  static constexpr bool kSums = true, kDot = true;
   __device__ static inline void scale_min(const uint8_t *blk, int s, int &sc, int &m) {
     const int a = blk[4 + (s & 3)], b = blk[8 + (s & 3)], c = blk[12 + (s & 3)];
     sc = s < 4 ? (a & 63) : ((c & 15) | ((a >> 6) << 4));
@@ -206,6 +249,7 @@ template <> struct Fmt<QG_Q4_K> {
 // with the half sums of x formed once per activation vector.
 template <> struct Fmt<QG_Q6_K> {
   static constexpr int kBytes = 210, kUnits = 8;
+  static constexpr bool kSums = true, kDot = true;
   template <typename P>
   __device__ static inline void codes(const P *blk, int u, uint32_t q[8]) {
     const int h = u >> 2, i = u & 3;
@@ -342,6 +386,15 @@ __device__ __forceinline__ void row_partial(const uint8_t *sb, int ph, int lane,
 #pragma unroll
       for (int t = 0; t < NT; ++t) s[t] = b < slice_n ? acc[t] : s[t];
     }
+  } else if constexpr (F::kDot) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int b = lane + 64 * c;
+      float acc[NT];
+      F::template dot<NT>(sb + ph + F::kBytes * b, xr[c], xs[c], s, acc);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s[t] = b < slice_n ? acc[t] : s[t];
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -376,8 +429,25 @@ __device__ __forceinline__ float row_partial(const uint8_t *sb, int ph, int lane
   return s[0];
 }
 
-// The unit input sums row_partial takes for the 32-weight formats, which use none.
-template <int C> __device__ constexpr float kNoSums[C][2] = {};
+// Each column's sums of its first and last 16 inputs, as row_partial takes
+// them for the formats that fold an offset (Q4_0) or a min (K-quants) out of
+// the dot; added in element order with no contraction of a producer's
+// multiply, so every kernel forms the same bits from the same inputs.
+template <int C>
+__device__ __forceinline__ void unit_sums(const float (&xr)[C][32], float (&xs)[C][2]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      lo += xr[c][e];
+      hi += xr[c][16 + e];
+    }
+    xs[c][0] = lo;
+    xs[c][1] = hi;
+  }
+}
 
 // Largest rows per chain tile, per (format, block columns per lane): a chain
 // wave holds its tile's fetched rows in registers until staged.
@@ -559,7 +629,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   // wave_sum63, the runs in column order -- the team's waves cover every
   // column, so no extra read), then one scale per input.
   float xr[C][NT][32];
-  float xs[C][NT][2];  // K-quants: the sums of each unit's first and last 16 inputs
+  float xs[C][NT][2];  // Q4_0, K-quants: the sums of each unit's first and last 16 inputs
   constexpr int in_op = op_in(OP);
   auto load_x = [&](const float *x, const float *x2) {
 #pragma unroll
@@ -609,7 +679,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
         for (int e = 0; e < 32; ++e) xr[c][0][e] *= inv;
       __syncthreads();  // ssq is read before a later window rewrites it
     }
-    if constexpr (Fmt<FMT>::kUnits > 1) {
+    if constexpr (Fmt<FMT>::kSums) {
       // Sums of the inputs as loaded: no multiply of a fused transform may
       // be contracted into these adds, or a fused launch would not give the
       // bits of the separate calls.
