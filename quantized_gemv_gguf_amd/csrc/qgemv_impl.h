@@ -198,10 +198,15 @@ template <> struct Fmt<QG_Q4_K> {
   template <int NT>
   __device__ static inline void dot(const uint8_t *blk, int s, const float (&x)[NT][32], const float (&xs)[NT][2],
                                     const float (&acc)[NT], float (&res)[NT]) {
-    uint32_t hd;
-    __builtin_memcpy(&hd, blk, 4);
-    int sc, m;
-    scale_min(blk, s, sc, m);
+    // d, dmin and the 12 scale bytes in one 16-byte read; this sub-block's
+    // three scale bytes are byte s & 3 of words 1, 2 and 3
+    uint32_t hw[4];
+    __builtin_memcpy(hw, blk, 16);
+    const uint32_t hd = hw[0];
+    const int sh = 8 * (s & 3);
+    const int a = (int)((hw[1] >> sh) & 0xffu), b = (int)((hw[2] >> sh) & 0xffu), c = (int)((hw[3] >> sh) & 0xffu);
+    const int sc = s < 4 ? (a & 63) : ((c & 15) | ((a >> 6) << 4));
+    const int m = s < 4 ? (b & 63) : ((c >> 4) | ((b >> 6) << 4));
     uint32_t q[8];
     __builtin_memcpy(q, blk + 16 + 32 * (s >> 1), 32);
     // codes of bytes 0 and 2 (then 1 and 3) of a word as two fp16 subnormals
