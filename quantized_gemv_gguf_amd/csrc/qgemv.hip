@@ -472,7 +472,8 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     const uint32_t last16 = ((ph + T.slice_len - 1) >> 4) << 4;
     const QG_GLOBAL uint8_t *pa = p - ph;
 #pragma unroll
-    for (int v = 0; v < V; ++v) buf[i][v] = *(const QG_GLOBAL u32x4 *)(pa + min(lane16 + 1024u * v, last16));
+    for (int v = 0; v < V; ++v)  // read once per pass: non-temporal, as the GEMV's copies
+      buf[i][v] = __builtin_nontemporal_load((const QG_GLOBAL u32x4 *)(pa + min(lane16 + 1024u * v, last16)));
   };
 
   // The 32 inputs of each block column SB wit + 64 c + lane, zero past the

@@ -495,9 +495,13 @@ constexpr int kGemvTileRows = 8;  // most rows per tile
 // with a scalar base, a 32-bit lane offset and the LDS destination in M0.
 // Written as inline assembly because the compiler's own waits for LDS DMA
 // drain every outstanding load before any LDS read; here the kernel counts
-// its loads and waits with s_waitcnt vmcnt itself.
+// its loads and waits with s_waitcnt vmcnt itself.  Weights are read once
+// per pass, so the loads carry the non-temporal hint (nt): on MI355X that
+// took the 44-layer Q8_0 pass from 4.17 to 4.02 ms per token (the
+// k = 24576 GEMV from 31.1 to 29.1 us).
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
