@@ -20,7 +20,8 @@ check of the GPU results against the oracle.
 Other workloads (--workload): q4_0_4096, moe_mxfp4, ffn_streamed, q8_0_256, and
 q4_k_m_dense20b (the same pass with Q4_K QKV/out/up and a Q6_K down
 projection, 12.9 GB), dense20b_batch (--batch tokens per step through
-qgemv_rows_batch).
+qgemv_rows_batch), moe_streamed (the MoE experts streamed from pinned host
+memory, ring and zero-copy).
 """
 from __future__ import annotations
 
@@ -758,6 +759,99 @@ def ffn_streamed_workload(args, dev):
                        "lookahead": c["lookahead"], "best_block_rows": int(best)}}
 
 
+def moe_streamed_workload(args, dev):
+    """The MXFP4 MoE workload with the expert tensors in pinned host memory
+    (the pages' setting: experts that do not fit the GPU are streamed): per
+    token the 8 gate/up windows of the 4 selected experts and then their 4
+    down windows go through the block ring (lookahead 1, i.e. two slots, and
+    lookahead 2) at block_rows 128, 512 and 2880 (whole experts), with SiLU*up
+    between; and the same token with the kernels reading the pinned experts
+    in place (mapped).
+    Rate = selected-expert bytes / wall time, against one 256 MiB pinned copy;
+    outputs compared bit for bit with the resident token."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    c = synth.CONFIGS[4]
+    E, out, k, ns = c["n_expert"], c["out"], c["k"], c["n_sel"]
+    rows = E * out
+    f32 = dict(dtype=torch.float32, device=dev)
+
+    def pinned(a):
+        t = torch.empty(a.shape, dtype=torch.uint8, pin_memory=True)
+        t.numpy()[...] = a
+        return t
+
+    host = [synth.blocks(q.MXFP4, rows, k, synth.seed_of(4, t)) for t in range(3)]
+    pin = [pinned(h) for h in host]
+    res = [torch.from_numpy(h).to(dev) for h in host]
+    del host
+    ids = synth.expert_ids(E, ns, c["tokens"], synth.seed_of(4, 8))
+    xs = torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(4, 100 + t)) for t in range(c["tokens"])])).to(dev)
+    gu, h, ye = torch.empty(2 * ns * out, **f32), torch.empty(ns * out, **f32), torch.empty(ns * out, **f32)
+    per_tok = 3 * ns * q.qgemv_weight_bytes(q.MXFP4, out, k)
+
+    def token(ws, t, streamer=None, B=0, mapped=False):
+        t = t % c["tokens"]
+        M = [q.Matrix(w, q.MXFP4, rows, k) for w in ws]
+        sel = [int(v) for v in ids[t]]
+        gw = [q.Window(M[m], e * out, (e + 1) * out, xs[t], gu[(m * ns + s) * out:(m * ns + s + 1) * out])
+              for m in range(2) for s, e in enumerate(sel)]
+        dw = [q.Window(M[2], e * out, (e + 1) * out, h[s * out:(s + 1) * out], ye[s * out:(s + 1) * out])
+              for s, e in enumerate(sel)]
+        if mapped:
+            q.qgemv_mapped_windows(gw)
+            q.qgemv_silu_mul(gu[:ns * out], gu[ns * out:], h)
+            q.qgemv_mapped_windows(dw)
+        elif streamer is None:
+            q.qgemv_windows(gw)
+            q.qgemv_silu_mul(gu[:ns * out], gu[ns * out:], h)
+            q.qgemv_windows(dw)
+        else:
+            streamer.windows(gw, B)
+            q.qgemv_silu_mul(gu[:ns * out], gu[ns * out:], h)
+            streamer.windows(dw, B)
+
+    n = max(args.steps, 16)
+    refs = []
+    for t in range(n):
+        token(res, t)
+        refs.append(ye.clone())
+    torch.cuda.synchronize()
+    big = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dbig = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dbig.copy_(big, non_blocking=True)
+    _, ms = _timed(lambda i: dbig.copy_(big, non_blocking=True), 5, torch)
+    link_256 = (256 << 20) * 5 / (ms / 1e3) / 1e9
+    rb = q.qgemv_weight_bytes(q.MXFP4, 1, k)
+    legs = {}
+
+    def measure(name, **kw):
+        for t in range(max(args.warmup, 1)):
+            token(pin, t, **kw)
+        torch.cuda.synchronize()
+        same = True
+        wall, _ = _timed(lambda i: token(pin, i, **kw), n, torch)
+        # bit identity on the last token, against the resident one
+        same = bool(torch.equal(ye.view(torch.int32), refs[(n - 1) % len(refs)].view(torch.int32)))
+        link = per_tok * n / wall / 1e9
+        legs[name] = {"link_GBs": link, "us_per_token": wall / n * 1e6, "pct_of_256MiB_copy": 100 * link / link_256,
+                      "bit_identical_to_resident": same}
+
+    for B in (128, 512, out):
+        for la in (1, 2):
+            with q.Streamer(B * rb, la) as st:
+                measure(f"ring_B{B}_lookahead{la}", streamer=st, B=B)
+                legs[f"ring_B{B}_lookahead{la}"]["ring_bytes"] = st.ring_bytes
+    measure("mapped", mapped=True)
+    best = max(legs, key=lambda kk: legs[kk]["link_GBs"])
+    return {"value": legs[best]["link_GBs"], "ms_per_step": legs[best]["us_per_token"] / 1e3,
+            "unit_note": "host-link GB/s of the selected experts' bytes per token (bytes / wall time)",
+            "bytes_per_token": per_tok, "h2d_256MiB_GBs": link_256, "legs": legs,
+            "config": {"workload": c["name"] + "_streamed", "format": "MXFP4", "n_expert": E, "out": out, "k": k,
+                       "experts_per_token": ns, "tokens": n, "best": best}}
+
+
 def q8_0_small_workload(args, dev):
     """Q8_0 256x1024: a launch-latency case (278 KB of weights)."""
     import torch
@@ -858,7 +952,8 @@ def kquant_dense_workload(args, dev):
 
 WORKLOADS = {"dense20b": dense_workload, "q4_0_4096": q4_0_workload, "moe_mxfp4": moe_workload,
              "ffn_streamed": ffn_streamed_workload, "q8_0_256": q8_0_small_workload,
-             "q4_k_m_dense20b": kquant_dense_workload, "dense20b_batch": dense_batch_workload}
+             "q4_k_m_dense20b": kquant_dense_workload, "dense20b_batch": dense_batch_workload,
+             "moe_streamed": moe_streamed_workload}
 
 
 # --- entry --------------------------------------------------------------------------

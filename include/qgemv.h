@@ -287,9 +287,12 @@ int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
  * stream and per-slot events (neurostream README, "The idea": blocks sized so
  * that lookahead + 1 buffers fit; "Bugs worth knowing about": the pipeline
  * holds depth + 1 blocks, because the block being multiplied keeps its
- * buffer until its output exists).  Block k is copied on the copy stream into
- * slot k mod (lookahead + 1) once the kernel of block k - lookahead - 1 has
- * released that slot; its kernel runs on the caller's stream after the copy. */
+ * buffer until its output exists).  Block k is copied into slot
+ * k mod (lookahead + 1) once the kernel of block k - lookahead - 1 has
+ * released that slot, on one of min(lookahead, 2) copy streams taken in turn
+ * (so that two copies can be in flight at once; the copy streams are shared
+ * by the process's streamers on a device and kept until it exits); its
+ * kernel runs on the caller's stream after the copy. */
 typedef struct qg_streamer qg_streamer;
 
 /* slot_bytes >= 1, lookahead >= 1.  Allocates (lookahead + 1) * slot_bytes of

@@ -964,13 +964,42 @@ int validate_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win
 // C ABI
 // ---------------------------------------------------------------------------
 
+namespace {
+// The streamers' copy streams: kCopyStreams non-blocking streams per device,
+// created on first use and kept until the process ends.
+constexpr int kCopyStreams = 2;
+
+hipError_t copy_pool(int device, hipStream_t **out) {
+  static std::mutex mu;
+  static hipStream_t pool[64][kCopyStreams] = {};
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  for (int i = 0; i < kCopyStreams; ++i)
+    if (!pool[device][i]) {
+      hipError_t e = hipStreamCreateWithFlags(&pool[device][i], hipStreamNonBlocking);
+      if (e != hipSuccess) {
+        pool[device][i] = nullptr;
+        return e;
+      }
+    }
+  *out = pool[device];
+  return hipSuccess;
+}
+}  // namespace
+
 struct qg_streamer {
   int device;
   int64_t slot_bytes;
   int64_t slot_stride;  // slot_bytes rounded up to 256 (slots stay 16-byte aligned)
   int lookahead;
   uint8_t *ring;
-  hipStream_t copy;
+  // Copy streams, used in turn by consecutive blocks (slot s takes stream
+  // s mod their count), so that two host->device copies can run at once.
+  // They come from a per-device pool created once per process: the runtime
+  // spreads streams over a few hardware queues as they are created, and
+  // streams made and dropped per streamer ended up sharing the caller's
+  // queue now and then, which serialised copies with kernels.
+  std::vector<hipStream_t> copies;
   std::vector<hipEvent_t> ready, freed;
   std::vector<char> freed_valid;
   uint64_t next;
@@ -1256,7 +1285,6 @@ int qgemv_stream_create(int64_t slot_bytes, int32_t lookahead, qg_streamer **out
   st->slot_stride = (slot_bytes + 255) / 256 * 256;
   st->lookahead = lookahead;
   st->ring = nullptr;
-  st->copy = nullptr;
   st->next = 0;
   const int n = lookahead + 1;
   auto fail = [&](hipError_t e, const char *what) {
@@ -1267,8 +1295,9 @@ int qgemv_stream_create(int64_t slot_bytes, int32_t lookahead, qg_streamer **out
   hipError_t e;
   if ((e = hipGetDevice(&st->device)) != hipSuccess) return fail(e, "hipGetDevice");
   if ((e = hipMalloc((void **)&st->ring, (size_t)st->slot_stride * n)) != hipSuccess) return fail(e, "hipMalloc(ring)");
-  if ((e = hipStreamCreateWithFlags(&st->copy, hipStreamNonBlocking)) != hipSuccess)
-    return fail(e, "hipStreamCreateWithFlags");
+  hipStream_t *pool = nullptr;
+  if ((e = copy_pool(st->device, &pool)) != hipSuccess) return fail(e, "hipStreamCreateWithFlags");
+  st->copies.assign(pool, pool + std::min(lookahead, kCopyStreams));
   st->ready.assign(n, nullptr);
   st->freed.assign(n, nullptr);
   st->freed_valid.assign(n, 0);
@@ -1292,7 +1321,8 @@ int qgemv_stream_destroy(qg_streamer *st) {
   if (!st) return QG_OK;
   int rc = QG_OK;
   hipError_t e;
-  if (st->copy && (e = hipStreamSynchronize(st->copy)) != hipSuccess) rc = hip_fail(e, "hipStreamSynchronize");
+  for (auto cs : st->copies)
+    if (cs && (e = hipStreamSynchronize(cs)) != hipSuccess && rc == QG_OK) rc = hip_fail(e, "hipStreamSynchronize");
   for (auto ev : st->freed)
     if (ev) {
       if ((e = hipEventSynchronize(ev)) != hipSuccess && rc == QG_OK) rc = hip_fail(e, "hipEventSynchronize");
@@ -1300,7 +1330,7 @@ int qgemv_stream_destroy(qg_streamer *st) {
     }
   for (auto ev : st->ready)
     if (ev) (void)hipEventDestroy(ev);
-  if (st->copy) (void)hipStreamDestroy(st->copy);
+  // (the copy streams belong to the per-device pool and stay)
   if (st->ring) (void)hipFree(st->ring);
   delete st;
   return rc;
@@ -1358,10 +1388,11 @@ int stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win
       const int64_t n = std::min(B, win[i].row_end - r);
       const int slot = (int)(st->next++ % (uint64_t)nslot);
       uint8_t *dst = st->ring + (int64_t)slot * st->slot_stride;
-      if (st->freed_valid[slot]) QG_HIP(hipStreamWaitEvent(st->copy, st->freed[slot], 0));
+      hipStream_t cs = st->copies[slot % st->copies.size()];
+      if (st->freed_valid[slot]) QG_HIP(hipStreamWaitEvent(cs, st->freed[slot], 0));
       QG_HIP(hipMemcpyAsync(dst, (const uint8_t *)win[i].data + r * rb, (size_t)(n * rb),
-                            hipMemcpyHostToDevice, st->copy));
-      QG_HIP(hipEventRecord(st->ready[slot], st->copy));
+                            hipMemcpyHostToDevice, cs));
+      QG_HIP(hipEventRecord(st->ready[slot], cs));
       QG_HIP(hipStreamWaitEvent(stream, st->ready[slot], 0));
       qg_window blk = {dst, n, 0, n, win[i].x, win[i].y + (r - win[i].row_start)};
       int rc = launch_gemv(fmt, k, &blk, 1, 0, stream);
