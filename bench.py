@@ -718,6 +718,21 @@ def ffn_streamed_workload(args, dev):
     run(res_w)
     torch.cuda.synchronize()
     ref = y.clone()
+    # resident, for reference: the separate first phase (gate/up grid, SiLU*up)
+    # against the SwiGLU pair grid (qgemv_rows_swiglu), each then down
+    Wr = [q.Matrix(res_w[0], q.Q8_0, F, H), q.Matrix(res_w[1], q.Q8_0, F, H), q.Matrix(res_w[2], q.Q8_0, H, F)]
+
+    def fused(i=0):
+        q.qgemv_rows_swiglu(Wr[0], Wr[1], 0, F, x, hh)
+        q.qgemv_rows(Wr[2], 0, H, hh, y)
+
+    resident = {}
+    for name, fn in (("separate", lambda i: run(res_w)), ("swiglu_pair", fused)):
+        for _ in range(max(args.warmup, 2)):
+            fn(0)
+        wall_r, _ = _timed(fn, 64, torch)
+        resident[name] = {"us_per_token": wall_r / 64 * 1e6, "GBs": per_tok * 64 / wall_r / 1e9,
+                          "bit_identical": bool(torch.equal(y.view(torch.int32), ref.view(torch.int32)))}
     # host link: one 256 MiB pinned copy, and copies of each block size
     big = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     dbig = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -755,6 +770,7 @@ def ffn_streamed_workload(args, dev):
     return {"value": out[best]["link_GBs"], "ms_per_step": out[best]["ms_per_token"], "unit_note":
             "host-link GB/s of the streamed pass (weight bytes copied / wall time)",
             "bytes_per_token": per_tok, "h2d_256MiB_GBs": link_256, "block_rows": out, "mapped": mapped,
+            "resident": resident,
             "config": {"workload": c["name"], "format": "Q8_0", "hidden": H, "ffn": F,
                        "lookahead": c["lookahead"], "best_block_rows": int(best)}}
 
