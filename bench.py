@@ -906,15 +906,21 @@ def dense_batch_workload(args, dev):
     c = synth.CONFIGS[cfg]
     layers = args.layers or c["layers"]
     B = args.batch
+    mfma = args.mfma
+    if mfma and args.kquant:
+        raise SystemExit("--mfma takes the Q8_0 pass (the matrix-core path has no K-quant decoder)")
     model = DensePass(layers, c["hidden"], c["ffn"], dev, cfg=cfg)
     H, F = c["hidden"], c["ffn"]
     X = {k: torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(10, 1000 * (k // 1024) + t))
                                         for t in range(B)])).to(dev) for k in (H, F)}
     Y = [torch.empty((B, r), dtype=torch.float32, device=dev) for _, r, _ in model.shapes]
     L, st = model.lib, model.stream
+    call = "qgemv_rows_mfma" if mfma else "qgemv_rows_batch"
 
     def passes(k):
         """Tokens per pass for this k (the library's choice, restated for the byte count)."""
+        if mfma:
+            return [min(16, B - t) for t in range(0, B, 16)]
         nb = k // 32
         wt1 = -(-nb // 64)
         c_ = 1 if (wt1 <= 12 and model.fmts[0] != q.Q4_0) else 2
@@ -928,9 +934,12 @@ def dense_batch_workload(args, dev):
 
     def step(_=0):
         for i, (mp, r, _, _, nbytes, k, m) in enumerate(model.calls):
-            rc = L.qgemv_rows_batch(mp, 0, r, X[k].data_ptr(), k, B, Y[m].data_ptr(), r, 0, st)
+            if mfma:
+                rc = L.qgemv_rows_mfma(mp, 0, r, X[k].data_ptr(), k, B, Y[m].data_ptr(), r, st)
+            else:
+                rc = L.qgemv_rows_batch(mp, 0, r, X[k].data_ptr(), k, B, Y[m].data_ptr(), r, 0, st)
             if rc != 0:
-                raise RuntimeError(f"qgemv_rows_batch failed: {rc}")
+                raise RuntimeError(f"{call} failed: {rc}")
 
     for _ in range(args.warmup):
         step()
@@ -954,9 +963,10 @@ def dense_batch_workload(args, dev):
     return {"value": per_step_read * args.steps / wall / 1e9, "ms_per_step": wall / args.steps * 1e3,
             "tokens_per_s": B * args.steps / wall, "token_equiv_GBs": tok_bytes * args.steps / wall / 1e9,
             "bytes_read_per_step": per_step_read, "weight_bytes_per_token": model.bytes_per_token,
-            "config": {"workload": c["name"] + f"_batch{B}", "layers": layers, "format": FMT_LABEL[cfg],
-                       "tokens_per_step": B, "passes_per_gemv": {str(k): passes(k) for k in (H, F)},
-                       "launch": "176 qgemv_rows_batch calls per step"},
+            "config": {"workload": c["name"] + f"_batch{B}" + ("_mfma" if mfma else ""), "layers": layers,
+                       "format": FMT_LABEL[cfg], "tokens_per_step": B,
+                       "passes_per_gemv": {str(k): passes(k) for k in (H, F)},
+                       "launch": f"176 {call} calls per step"},
             "parity": {"rows_checked": 16 * 4 * B, "max_componentwise": worst, "tol": TOL,
                        "pass": bool(worst <= TOL)}}
 
@@ -992,6 +1002,8 @@ def main(argv=None):
     p.add_argument("--block-rows", type=int, default=0, help="block_rows for the MoE workload")
     p.add_argument("--batch", type=int, default=4, help="tokens per step of dense20b_batch")
     p.add_argument("--kquant", action="store_true", help="dense20b_batch in the Q4_K_M mix")
+    p.add_argument("--mfma", action="store_true",
+                   help="dense20b_batch through qgemv_rows_mfma (fp32 matrix cores, 16 tokens per pass)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a 256 MiB device-to-device copy (a kernel of known traffic, to scale HBM counters)")
     args = p.parse_args(argv)

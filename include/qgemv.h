@@ -170,6 +170,21 @@ int qgemv_rows_batch(const qg_matrix *w, int64_t row_start, int64_t row_end,
                      const float *x, int64_t x_stride, int32_t n_tok, float *y,
                      int64_t y_stride, int64_t block_rows, qg_stream_t stream);
 
+/* Rows [row_start, row_end) of w for n_tok tokens at once on the fp32 matrix
+ * cores: y_t[r - row_start] = sum_c W[r][c] x_t[c].  With several tokens the
+ * product is a dense contraction over the shared weights (neurostream README,
+ * "What the numbers taught us": tokens that share one pass over the weights
+ * cost about one token's weight traffic); passes of 16 tokens each read the
+ * weights once.  Formats QG_Q8_0, QG_Q4_0, QG_MXFP4 (else QG_E_FMT).  x, y:
+ * device, token t at x + t x_stride and y + t y_stride (y_stride >=
+ * row_end - row_start when n_tok > 1).  Each weight is formed exactly in fp32
+ * and the sums are fp32, in the matrix cores' order: y_t is within fp32
+ * rounding of W x_t, not bit-identical to qgemv_rows (qgemv_rows_batch is).
+ * n_tok = 0 or an empty window does nothing; other errors as qgemv_rows_batch. */
+int qgemv_rows_mfma(const qg_matrix *w, int64_t row_start, int64_t row_end,
+                    const float *x, int64_t x_stride, int32_t n_tok, float *y,
+                    int64_t y_stride, qg_stream_t stream);
+
 enum qg_in_op { QG_IN_X = 0, QG_IN_RMS = 1, QG_IN_GELU_RMS = 2, QG_IN_SILU_MUL = 3 };
 enum qg_out_op { QG_OUT_Y = 0, QG_OUT_GELU = 1 };
 

@@ -83,6 +83,7 @@ def lib():
         "qgemv_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_rows_batch": ([P(qg_matrix), _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i64, _vp], ctypes.c_int),
+        "qgemv_rows_mfma": ([P(qg_matrix), _i64, _i64, _vp, _i64, _i32, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_expert_windows_op": ([P(qg_matrix), _i32, _i64, P(_i32), _i32, _vp, _vp, _i64, _i32, ctypes.c_float,
                                      _i32, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_combine": ([_vp, _i64, _i32, _vp, _i64, _vp, _vp], ctypes.c_int),
@@ -243,6 +244,23 @@ def qgemv_rows_batch(w: Matrix, row_start: int, row_end: int, x, y, block_rows: 
     _f32(y, 0, "y")
     _check(lib().qgemv_rows_batch(ctypes.byref(m), row_start, row_end, _ptr(x), x.stride(0), nt, _ptr(y),
                                   y.stride(0), block_rows, _stream(stream)), "qgemv_rows_batch")
+
+
+def qgemv_rows_mfma(w: Matrix, row_start: int, row_end: int, x, y, stream=None) -> None:
+    """As qgemv_rows_batch on the fp32 matrix cores (Q8_0, Q4_0, MXFP4): y[t]
+    within fp32 rounding of W[row_start:row_end] . x[t], not bit-identical to
+    the one-token calls."""
+    m = w.c()
+    n = max(row_end - row_start, 0)
+    if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
+        raise ValueError("x and y must be (n_tok, ...) with the same n_tok")
+    if x.stride(1) != 1 or y.stride(1) != 1 or x.shape[1] < w.k or y.shape[1] < n:
+        raise ValueError("rows of x (k floats) and y (one per output row) must be contiguous")
+    nt = x.shape[0]
+    _f32(x, 0, "x")
+    _f32(y, 0, "y")
+    _check(lib().qgemv_rows_mfma(ctypes.byref(m), row_start, row_end, _ptr(x), x.stride(0), nt, _ptr(y),
+                                 y.stride(0), _stream(stream)), "qgemv_rows_mfma")
 
 
 def qgemv_windows(windows: Sequence[Window], block_rows: int = 0, stream=None, fmt=None, k=None) -> None:

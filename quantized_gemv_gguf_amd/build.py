@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 # qgemv.hip: chain kernel, small kernels and the C ABI; gemv_op*.hip: one
 # fused-transform variant of the GEMV kernel each (all formats and team shapes),
 # compiled in parallel and linked into one library.
-SOURCES = ["qgemv.hip"] + [f"gemv_op{i}.hip" for i in range(7)] + ["gemv_batch.hip"]
+SOURCES = ["qgemv.hip"] + [f"gemv_op{i}.hip" for i in range(7)] + ["gemv_batch.hip", "gemv_mfma.hip"]
 HEADERS = ["qgemv_impl.h"]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqgemv.so")

@@ -1077,6 +1077,35 @@ int qgemv_rows_batch(const qg_matrix *w, int64_t row_start, int64_t row_end, con
   return QG_OK;
 }
 
+int qgemv_rows_mfma(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, int64_t x_stride,
+                    int32_t n_tok, float *y, int64_t y_stride, qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  const int64_t n = row_end - row_start;
+  if (w->fmt != QG_Q8_0 && w->fmt != QG_Q4_0 && w->fmt != QG_MXFP4) return QG_E_FMT;
+  if (n_tok < 0 || x_stride < 0 || (n_tok > 1 && y_stride < n)) return QG_E_ARG;
+  if (n == 0 || n_tok == 0) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  const int64_t rb = row_bytes_of(w->fmt, w->k);
+  MfmaArgs a;
+  a.w = (const uint8_t *)w->data + row_start * rb;
+  a.row_bytes = rb;
+  a.n_rows = n;
+  a.x_stride = x_stride;
+  a.y_stride = y_stride;
+  a.nb = (int32_t)(w->k / 32);
+  // passes of 16 tokens, each reading the weights once
+  for (int32_t t = 0; t < n_tok; t += 16) {
+    a.x = x + (int64_t)t * x_stride;
+    a.y = y + (int64_t)t * y_stride;
+    a.n_tok = std::min<int32_t>(16, n_tok - t);
+    if ((rc = launch_gemv_mfma(w->fmt, a, (hipStream_t)stream))) return rc;
+    QG_HIP(hipGetLastError());
+  }
+  return QG_OK;
+}
+
 int qgemv_rows_op(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, const float *x2,
                   int32_t in_op, float eps, int32_t out_op, float *y, int64_t block_rows, qg_stream_t stream) {
   int rc = check_matrix(w);

@@ -333,6 +333,20 @@ struct GemvArgs {
   int64_t x_stride, y_stride;
 };
 
+// Up to 16 tokens on the matrix cores (gemv_mfma.hip): rows [0, n_rows) of a
+// matrix whose row r starts at w + r row_bytes; token t < n_tok reads
+// x + t x_stride and writes y + t y_stride.
+struct MfmaArgs {
+  const uint8_t *w;
+  const float *x;
+  float *y;
+  int64_t row_bytes, n_rows, x_stride, y_stride;
+  int32_t nb, n_tok;
+};
+// Enqueues the launch (Q8_0, Q4_0, MXFP4; else QG_E_FMT); the caller checks
+// the launch status.
+int launch_gemv_mfma(int32_t fmt, const MfmaArgs &a, hipStream_t stream);
+
 // Sum over the 64 lanes of a wave in a fixed order (DPP row shifts, then row
 // broadcasts); the total lands in lane 63.
 template <int CTRL, int ROW_MASK, int BANK_MASK>

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -220,6 +220,29 @@ def test_rows_batch_validation():
     assert call(nt=0, x=0, y=0) == 0
     assert call(r0=3, r1=3, x=0, y=0) == 0
     # one token needs no y stride
+    assert call(nt=1, ys=0, x=0) == E_NULL
+
+
+def test_rows_mfma_validation():
+    L = q.lib()
+
+    def call(m=None, r0=0, r1=8, x=FAKE, xs=64, nt=2, y=FAKE, ys=8):
+        m = mat() if m is None else m
+        return L.qgemv_rows_mfma(ctypes.byref(m), r0, r1, x, xs, nt, y, ys, None)
+
+    assert L.qgemv_rows_mfma(None, 0, 8, FAKE, 64, 2, FAKE, 8, None) == E_NULL
+    assert call(m=mat(fmt=6)) == E_FMT
+    # K-quants have no matrix-core decoder here
+    assert call(m=mat(fmt=q.Q4_K, k=256, nbytes=8 * 144)) == E_FMT
+    assert call(m=mat(fmt=q.Q6_K, k=256, nbytes=8 * 210)) == E_FMT
+    assert call(m=mat(k=48, nbytes=0)) == E_SHAPE
+    assert call(r1=9) == E_RANGE
+    assert call(nt=-1) == E_ARG
+    assert call(xs=-1) == E_ARG
+    assert call(ys=7) == E_ARG
+    assert call(x=0) == E_NULL and call(y=0) == E_NULL
+    assert call(nt=0, x=0, y=0) == 0
+    assert call(r0=3, r1=3, x=0, y=0) == 0
     assert call(nt=1, ys=0, x=0) == E_NULL
 
 
