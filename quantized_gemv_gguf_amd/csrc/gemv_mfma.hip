@@ -18,14 +18,15 @@
 // W x but is not bit-identical to the one-token kernels' results.
 //
 // Work split: a workgroup of WT waves owns RT tiles of 16 rows; its waves
-// take the row blocks' 32-weight blocks in turn (wave w: blocks w, w + WT, ...)
-// so that neighbouring waves read neighbouring bytes of each row, and the
+// take the rows' blocks in turn (the LDS kernel: chunks of kCB blocks, wave
+// w: chunks w, w + WT, ...; the register kernel: single blocks), and the
 // waves' partial sums are added in wave order through LDS.
 #include "qgemv_impl.h"
 
 namespace qgemv_detail {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef u32x4 __attribute__((aligned(1))) u32x4_u1;  // 16 bytes at any address
 
 template <int FMT> struct MfmaFmt;
 
@@ -35,7 +36,7 @@ template <int FMT> struct MfmaFmt;
 
 // Q8_0: fp16 d, 32 int8 codes (RAMforge README, "Milestone 5").
 template <> struct MfmaFmt<QG_Q8_0> {
-  static constexpr int kBytes = 34;
+  static constexpr int kBytes = 34, kCB = 8;  // kCB blocks: 17 granules of 16 bytes
   struct Raw { uint32_t h; uint2 q; };
   // x offsets of the lane group's two runs of four positions
   __device__ static inline int x0(int g) { return 8 * g; }
@@ -57,7 +58,7 @@ template <> struct MfmaFmt<QG_Q8_0> {
 // Q4_0: fp16 d, 16 bytes; position j < 16 is the low nibble of byte j,
 // j + 16 its high nibble; w = d (q - 8) (RAMforge README, "Milestone 5").
 template <> struct MfmaFmt<QG_Q4_0> {
-  static constexpr int kBytes = 18;
+  static constexpr int kBytes = 18, kCB = 16;  // 18 granules
   struct Raw { uint32_t h, q; };
   __device__ static inline int x0(int g) { return 4 * g; }
   __device__ static inline int x1(int g) { return 16 + 4 * g; }
@@ -78,7 +79,7 @@ template <> struct MfmaFmt<QG_Q4_0> {
 // MXFP4: E8M0 e, 16 bytes of E2M1 codes in the Q4_0 nibble order;
 // w = 2^(e-127) E2M1(q), e = 255 is NaN (neurostream README, "The idea").
 template <> struct MfmaFmt<QG_MXFP4> {
-  static constexpr int kBytes = 17;
+  static constexpr int kBytes = 17, kCB = 16;  // 17 granules
   struct Raw { uint32_t e, q; };
   __device__ static inline int x0(int g) { return 4 * g; }
   __device__ static inline int x1(int g) { return 16 + 4 * g; }
@@ -204,15 +205,161 @@ __global__ void __launch_bounds__(64 * WT) gemv_mfma_kernel(const MfmaArgs a) {
   }
 }
 
-// Two 16-row tiles per workgroup (each x value loaded once for 32 rows), 8
-// waves, 2 blocks per round: of the shapes measured on the 20B-class pass
-// (1-2 tiles, 8-16 waves, 2-8 blocks per round) the fastest.
+// The same product with the weights staged through LDS.  A wave's k range
+// is a run of chunks of kCB blocks (wave w: chunks w, w + WT, ...); a chunk
+// of one row is GR 16-byte granules, and the wave reads its 16 RT rows' chunk
+// with contiguous 16-byte loads (lane l of load v: granule 64 v + l, in row
+// order), so each load instruction covers whole cache lines.  The granules
+// land in the wave's own LDS region (row stride an odd number of granules,
+// so the 16 rows of a tile fall in distinct banks) and the lanes read their
+// MFMA operands back from there; the next chunk's loads are in flight while
+// the current chunk is multiplied, and each block's x two blocks ahead.
+template <int FMT, int RT, int WT>
+__global__ void __launch_bounds__(64 * WT) gemv_mfma_lds_kernel(const MfmaArgs a) {
+  using F = MfmaFmt<FMT>;
+  using Raw = typename F::Raw;
+  constexpr int CB = F::kCB;
+  constexpr int CBYTES = CB * F::kBytes;  // bytes of a row's chunk
+  static_assert(CBYTES % 16 == 0, "a row's chunk is whole granules");
+  constexpr int GR = CBYTES / 16;         // granules per row's chunk
+  constexpr int GRP = GR | 1;             // LDS row stride in granules
+  constexpr int ROWS = 16 * RT;
+  constexpr int NG = ROWS * GR;           // granules per chunk
+  constexpr int NV = (NG + 63) / 64;      // loads per lane per chunk
+  constexpr int STAGE = ROWS * GRP * 16;  // LDS bytes per wave
+  constexpr int RED = WT * RT * 64 * 16;  // the final reduction's bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[(WT * STAGE > RED) ? WT * STAGE : RED];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15;  // A: tile row; B, D: token
+  const int g = lane >> 4;  // lane group: the block positions of the lane
+  const int nb = a.nb;
+  const int64_t rb = a.row_bytes;
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  uint8_t *stage = lds + wave * STAGE;
+
+  // This lane's granules of every chunk: row base and offset within the
+  // chunk, and the LDS slot.  Rows past the window read its last row.
+  const uint8_t *gbase[NV];
+  uint32_t goff[NV], gslot[NV];
+  bool gon[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int G = 64 * v + lane;
+    const int row = G / GR, q = G - (G / GR) * GR;
+    // (a lane past the chunk's granules loads granule 0 and stores nothing)
+    gon[v] = G < NG;
+    gbase[v] = a.w + min(r0 + (gon[v] ? row : 0), a.n_rows - 1) * rb;
+    goff[v] = gon[v] ? 16u * (uint32_t)q : 0u;  // + 16 <= CBYTES
+    gslot[v] = 16u * (uint32_t)(row * GRP + q);
+  }
+  // Chunk c holds blocks [CB c, CB c + CB) of the row; the last one, when nb
+  // is not a multiple of CB, is moved back to end at the row's end (nb >= CB:
+  // the host's choice), so every load stays inside the row, and its blocks
+  // below CB c, counted in the chunk before, are zeroed.
+  const int nch = (nb + CB - 1) / CB;            // chunks of the row
+  const int mine = nch > wave ? (nch - wave + WT - 1) / WT : 0;  // this wave's chunks
+  auto chunk_base = [&](int c) { return min(CB * c, nb - CB); };
+  u32x4 gr[NV];
+  auto fetch = [&](int c) {
+    const int64_t off = (int64_t)chunk_base(c) * F::kBytes;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) gr[v] = *reinterpret_cast<const u32x4_u1 *>(gbase[v] + off + goff[v]);
+  };
+  const bool tok = i < a.n_tok;
+  const float *xp = a.x + (int64_t)(tok ? i : 0) * a.x_stride;
+  const int xo0 = F::x0(g), xo1 = F::x1(g);
+  // x of the wave's u-th block (u counts blocks over the wave's chunks; past
+  // its last chunk, zeros)
+  auto xload = [&](int u, float (&xv)[8]) {
+    const int c = wave + WT * (u / CB);
+    const int bb = chunk_base(c) + (u % CB);
+    const bool ok = bb >= CB * c && tok;
+    float4 p = float4{0.0f, 0.0f, 0.0f, 0.0f}, q = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tok) {
+      __builtin_memcpy(&p, xp + 32 * bb + xo0, 16);
+      __builtin_memcpy(&q, xp + 32 * bb + xo1, 16);
+    }
+    xv[0] = ok ? p.x : 0.0f;
+    xv[1] = ok ? p.y : 0.0f;
+    xv[2] = ok ? p.z : 0.0f;
+    xv[3] = ok ? p.w : 0.0f;
+    xv[4] = ok ? q.x : 0.0f;
+    xv[5] = ok ? q.y : 0.0f;
+    xv[6] = ok ? q.z : 0.0f;
+    xv[7] = ok ? q.w : 0.0f;
+  };
+
+  f32x4 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (mine > 0) {
+    float xr[4][8];  // x ring: block u in slot u % 4 (CB is a multiple of 4)
+    fetch(wave);
+    xload(0, xr[0]);
+    xload(1, xr[1]);
+    for (int n = 0; n < mine; ++n) {
+      // chunk n's granules to LDS (the previous chunk's reads are done: one
+      // wave's LDS operations complete in order), then chunk n + 1's loads
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if (gon[v]) *reinterpret_cast<u32x4 *>(stage + gslot[v]) = gr[v];
+      if (n + 1 < mine) fetch(wave + WT * (n + 1));
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int u = CB * n + c;
+        xload(u + 2, xr[(c + 2) & 3]);
+        const int cw = wave + WT * n;
+        const bool ok = chunk_base(cw) + c >= CB * cw;
+        Raw rw[RT];
+        float sc[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          rw[t] = F::load(stage + (16 * t + i) * (GRP * 16) + c * F::kBytes, g);
+          sc[t] = ok ? F::scale(rw[t]) : 0.0f;
+        }
+        mfma_steps<FMT, 0, RT>(rw, sc, xr[c & 3], acc);
+      }
+    }
+  }
+
+  // Add the waves' sums in wave order (the staging area is reused);
+  // thread q stores token q / (16 RT), tile row q % (16 RT), so consecutive
+  // threads write consecutive rows.
+  __syncthreads();
+  f32x4 *red = reinterpret_cast<f32x4 *>(lds);  // [WT][RT][64]
+#pragma unroll
+  for (int t = 0; t < RT; ++t) red[(wave * RT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  for (int q = threadIdx.x; q < 256 * RT; q += 64 * WT) {
+    const int j = q / (16 * RT), rr = q % (16 * RT);
+    const int t = rr >> 4, ii = rr & 15;
+    const int64_t r = r0 + rr;
+    if (j < a.n_tok && r < a.n_rows) {
+      const int l = j + 16 * (ii >> 2), e = ii & 3;
+      float s = red[t * 64 + l][e];
+#pragma unroll
+      for (int v = 1; v < WT; ++v) s += red[(v * RT + t) * 64 + l][e];
+      a.y[(int64_t)j * a.y_stride + r] = s;
+    }
+  }
+}
+
+// Launch shape: two 16-row tiles per workgroup (each x value loaded once for
+// 32 rows) and 8 waves; of the shapes measured on the 20B-class pass (1-2
+// tiles, 4-16 waves, with and without LDS staging) the fastest.  A matrix
+// shorter than one chunk (k < 32 kCB) takes the register kernel.
 template <int FMT>
 static int launch_fmt(const MfmaArgs &a, hipStream_t stream) {
-  constexpr int RT = 2, WT = 8, P = 2;
+  constexpr int RT = 2, WT = 8;
   const int64_t tiles = (a.n_rows + 16 * RT - 1) / (16 * RT);
   if (tiles > 0x7fffffff) return QG_E_SHAPE;
-  hipLaunchKernelGGL((gemv_mfma_kernel<FMT, RT, WT, P>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
+  if (a.nb >= MfmaFmt<FMT>::kCB)
+    hipLaunchKernelGGL((gemv_mfma_lds_kernel<FMT, RT, WT>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, RT, WT, 2>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
   return QG_OK;
 }
 

@@ -30,10 +30,12 @@ def sync():
     torch.cuda.synchronize()
 
 
-# (format, rows, k): whole and ragged 16-row tiles, k from one block per wave
-# (k = 256: 8 blocks for 8 waves) to several rounds with a ragged last one
-SHAPES = [(q.Q8_0, 300, 6144), (q.Q8_0, 17, 24576), (q.Q8_0, 64, 256), (q.Q8_0, 5, 96),
-          (q.Q4_0, 257, 4096), (q.Q4_0, 33, 2080), (q.MXFP4, 200, 2880), (q.MXFP4, 16, 32)]
+# (format, rows, k): whole and ragged 32-row workgroup tiles; the LDS-staged
+# kernel with one chunk (Q8_0 k = 256), whole chunks, and a last chunk moved
+# back over its predecessor (Q8_0 and Q4_0 k = 2080, MXFP4 k = 2880); the
+# register kernel below one chunk (Q8_0 k = 96, Q4_0 k = 480, MXFP4 k = 32)
+SHAPES = [(q.Q8_0, 300, 6144), (q.Q8_0, 17, 24576), (q.Q8_0, 64, 256), (q.Q8_0, 50, 2080), (q.Q8_0, 5, 96),
+          (q.Q4_0, 257, 4096), (q.Q4_0, 33, 2080), (q.Q4_0, 20, 480), (q.MXFP4, 200, 2880), (q.MXFP4, 16, 32)]
 
 
 def oracle_tokens(fmt, w, rows, k, xs):
