@@ -158,3 +158,35 @@ def test_mfma_noops_and_errors(dev):
     y2 = torch.empty((2, rows + 1), dtype=torch.float32, device=dev)
     with pytest.raises(q.QgemvError):
         q.qgemv_rows_mfma(M, 0, rows + 1, x, y2)
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0, q.MXFP4])
+def test_mfma_largest_k_single_row_and_shared_x(dev, fmt):
+    """k = QG_MAX_K (49152; 1536 blocks, the last Q4_0/MXFP4 chunk whole,
+    Q8_0's 192 chunks over 8 waves), a one-row window (31 clamped rows in its
+    tile), and x_stride = 0: every token reads the same x, so the 16 results
+    of a row are the same sums and must agree to the gates with the oracle."""
+    import torch
+    k, rows = 49152, 40
+    w = synth.blocks(fmt, rows, k, synth.seed_of(31, 70 + fmt))
+    M = q.Matrix(dput(w, dev), fmt, rows, k)
+    xs = np.stack([synth.x_vec(k, synth.seed_of(31, 500 + t)) for t in range(16)])
+    ref, a = oracle_tokens(fmt, w, rows, k, xs)
+    y = torch.full((16, rows), float("nan"), dtype=torch.float32, device=dev)
+    q.qgemv_rows_mfma(M, 0, rows, dput(xs, dev), y)
+    y1 = torch.full((16, 1), float("nan"), dtype=torch.float32, device=dev)
+    q.qgemv_rows_mfma(M, 23, 24, dput(xs, dev), y1)
+    X0 = dput(xs[:1], dev)
+    ys = torch.full((16, rows), float("nan"), dtype=torch.float32, device=dev)
+    import ctypes
+    m = M.c()
+    rc = q.lib().qgemv_rows_mfma(ctypes.byref(m), 0, rows, X0.data_ptr(), 0, 16, ys.data_ptr(), rows, None)
+    assert rc == 0
+    sync()
+    got, got1, gots = y.cpu().numpy(), y1.cpu().numpy(), ys.cpu().numpy()
+    for t in range(16):
+        check(got[t], ref[t], a[t], what=f"token {t}")
+        check(got1[t], ref[t, 23:24], a[t, 23:24], what=f"one row, token {t}")
+        check(gots[t], ref[0], a[0], what=f"shared x, token {t}")
+    # the same x and the same launch give the same sums for every token
+    assert np.array_equal(gots, np.broadcast_to(gots[0], gots.shape))
