@@ -1,5 +1,5 @@
 // gemv_mfma.hip -- the GEMV of up to 16 tokens at once on gfx950's fp32
-// matrix cores (v_mfma_f32_16x16x4_f32), for the 32-weight formats.
+// matrix cores (v_mfma_f32_16x16x4_f32), for Q8_0, Q4_0, MXFP4 and Q4_K.
 //
 // With 16 tokens the product Y = W X is a dense contraction (16 rows x 16
 // tokens x k per tile), so it goes to the matrix cores; the weights are still
@@ -49,6 +49,7 @@ template <> struct MfmaFmt<QG_Q8_0> {
     r.h = hb;
     return r;
   }
+  __device__ static inline Raw load_unit(const uint8_t *row, int c, int g) { return load(row + c * kBytes, g); }
   __device__ static inline float scale(const Raw &r) { return __half2float(__ushort_as_half((uint16_t)r.h)); }
   template <int S> __device__ static inline float w(const Raw &r, float d) {
     return d * (float)(int8_t)((S < 4 ? r.q.x : r.q.y) >> (8 * (S & 3)));
@@ -70,6 +71,7 @@ template <> struct MfmaFmt<QG_Q4_0> {
     r.h = hb;
     return r;
   }
+  __device__ static inline Raw load_unit(const uint8_t *row, int c, int g) { return load(row + c * kBytes, g); }
   __device__ static inline float scale(const Raw &r) { return __half2float(__ushort_as_half((uint16_t)r.h)); }
   template <int S> __device__ static inline float w(const Raw &r, float d) {
     return d * (float)((int)((r.q >> (8 * (S & 3) + 4 * (S >> 2))) & 15u) - 8);
@@ -89,6 +91,7 @@ template <> struct MfmaFmt<QG_MXFP4> {
     r.e = blk[0];
     return r;
   }
+  __device__ static inline Raw load_unit(const uint8_t *row, int c, int g) { return load(row + c * kBytes, g); }
   // 2^(e-127) as an fp32 bit pattern: normal for e >= 1, the subnormal
   // 2^-127 for e = 0
   __device__ static inline float scale(const Raw &r) {
@@ -97,6 +100,41 @@ template <> struct MfmaFmt<QG_MXFP4> {
   // E2M1 value of byte S & 3's low (S < 4) or high nibble (scale 1: exact)
   template <int S> __device__ static inline float w(const Raw &r, float sc) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q, 1.0f, S & 3)[S >> 2] * sc;
+  }
+};
+
+// Q4_K: 144-byte super-blocks of 8 units of 32 weights (fp16 d, fp16 dmin,
+// 12 bytes of 6-bit scales and mins, 128 bytes of nibbles); unit s's weights
+// are d sc_s q - dmin m_s, q the low (even s) or high (odd s) nibbles of bytes
+// 32 (s / 2) .. 32 (s / 2) + 31 (RAMforge README, "Milestone 5", Q4_K line).
+// Here kBytes is the bytes per unit (144 / 8), so a chunk of 8 units is one
+// super-block of 9 granules; k is a multiple of 256, so no chunk is ever
+// moved back and every unit's gate is 1.  The weight d sc q - dmin m is one
+// fused multiply-add of exact products, rounded once, as the oracle's.
+template <> struct MfmaFmt<QG_Q4_K> {
+  static constexpr int kBytes = 18, kCB = 8;
+  struct Raw { uint2 q; float dsc, dm; uint32_t sh; };
+  __device__ static inline int x0(int g) { return 8 * g; }
+  __device__ static inline int x1(int g) { return 8 * g + 4; }
+  __device__ static inline Raw load_unit(const uint8_t *row, int c, int g) {
+    const uint8_t *sb = row + (c >> 3) * 144;
+    const int s = c & 7;
+    int sc, m;
+    Fmt<QG_Q4_K>::scale_min(sb, s, sc, m);
+    uint16_t hd, hm;
+    __builtin_memcpy(&hd, sb, 2);
+    __builtin_memcpy(&hm, sb + 2, 2);
+    Raw r;
+    r.dsc = __half2float(__ushort_as_half(hd)) * (float)sc;
+    r.dm = __half2float(__ushort_as_half(hm)) * (float)m;
+    __builtin_memcpy(&r.q, sb + 16 + 32 * (s >> 1) + 8 * g, 8);
+    r.sh = 4u * (uint32_t)(s & 1);
+    return r;
+  }
+  __device__ static inline float scale(const Raw &) { return 1.0f; }
+  template <int S> __device__ static inline float w(const Raw &r, float gate) {
+    const float q = (float)(((S < 4 ? r.q.x : r.q.y) >> (8 * (S & 3) + r.sh)) & 15u);
+    return gate * fmaf(r.dsc, q, -r.dm);
   }
 };
 
@@ -317,7 +355,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_mfma_lds_kernel(const MfmaArgs a
         float sc[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-          rw[t] = F::load(stage + (16 * t + i) * (GRP * 16) + c * F::kBytes, g);
+          rw[t] = F::load_unit(stage + (16 * t + i) * (GRP * 16), c, g);
           sc[t] = ok ? F::scale(rw[t]) : 0.0f;
         }
         mfma_steps<FMT, 0, RT>(rw, sc, xr[c & 3], acc);
@@ -356,10 +394,11 @@ static int launch_fmt(const MfmaArgs &a, hipStream_t stream) {
   constexpr int RT = 2, WT = 8;
   const int64_t tiles = (a.n_rows + 16 * RT - 1) / (16 * RT);
   if (tiles > 0x7fffffff) return QG_E_SHAPE;
-  if (a.nb >= MfmaFmt<FMT>::kCB)
+  if (a.nb >= MfmaFmt<FMT>::kCB) {
     hipLaunchKernelGGL((gemv_mfma_lds_kernel<FMT, RT, WT>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
-  else
+  } else if constexpr (FMT != QG_Q4_K) {  // (a Q4_K row is at least one chunk)
     hipLaunchKernelGGL((gemv_mfma_kernel<FMT, RT, WT, 2>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
+  }
   return QG_OK;
 }
 
@@ -368,6 +407,7 @@ int launch_gemv_mfma(int32_t fmt, const MfmaArgs &a, hipStream_t stream) {
     case QG_Q8_0: return launch_fmt<QG_Q8_0>(a, stream);
     case QG_Q4_0: return launch_fmt<QG_Q4_0>(a, stream);
     case QG_MXFP4: return launch_fmt<QG_MXFP4>(a, stream);
+    case QG_Q4_K: return launch_fmt<QG_Q4_K>(a, stream);
     default: return QG_E_FMT;
   }
 }
