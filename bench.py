@@ -907,8 +907,6 @@ def dense_batch_workload(args, dev):
     layers = args.layers or c["layers"]
     B = args.batch
     mfma = args.mfma
-    if mfma and args.kquant:
-        raise SystemExit("--mfma takes the Q8_0 pass (the matrix-core path has no K-quant decoder)")
     model = DensePass(layers, c["hidden"], c["ffn"], dev, cfg=cfg)
     H, F = c["hidden"], c["ffn"]
     X = {k: torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(10, 1000 * (k // 1024) + t))

@@ -175,8 +175,8 @@ int qgemv_rows_batch(const qg_matrix *w, int64_t row_start, int64_t row_end,
  * product is a dense contraction over the shared weights (neurostream README,
  * "What the numbers taught us": tokens that share one pass over the weights
  * cost about one token's weight traffic); passes of 16 tokens each read the
- * weights once.  Formats QG_Q8_0, QG_Q4_0, QG_MXFP4, QG_Q4_K (else
- * QG_E_FMT; Q4_K's weight d sc q - dmin m is formed with one rounding).  x, y:
+ * weights once.  Every format (Q4_K's weight d sc q - dmin m is formed with
+ * one rounding, the others' exactly).  x, y:
  * device, token t at x + t x_stride and y + t y_stride (y_stride >=
  * row_end - row_start when n_tok > 1).  Each weight is formed exactly in fp32
  * and the sums are fp32, in the matrix cores' order: y_t is within fp32

@@ -247,7 +247,7 @@ def qgemv_rows_batch(w: Matrix, row_start: int, row_end: int, x, y, block_rows: 
 
 
 def qgemv_rows_mfma(w: Matrix, row_start: int, row_end: int, x, y, stream=None) -> None:
-    """As qgemv_rows_batch on the fp32 matrix cores (Q8_0, Q4_0, MXFP4, Q4_K): y[t]
+    """As qgemv_rows_batch on the fp32 matrix cores (every format): y[t]
     within fp32 rounding of W[row_start:row_end] . x[t], not bit-identical to
     the one-token calls."""
     m = w.c()

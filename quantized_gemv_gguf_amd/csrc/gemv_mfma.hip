@@ -1,5 +1,5 @@
 // gemv_mfma.hip -- the GEMV of up to 16 tokens at once on gfx950's fp32
-// matrix cores (v_mfma_f32_16x16x4_f32), for Q8_0, Q4_0, MXFP4 and Q4_K.
+// matrix cores (v_mfma_f32_16x16x4_f32), for every format.
 //
 // With 16 tokens the product Y = W X is a dense contraction (16 rows x 16
 // tokens x k per tile), so it goes to the matrix cores; the weights are still
@@ -138,6 +138,40 @@ template <> struct MfmaFmt<QG_Q4_K> {
   }
 };
 
+// Q6_K: 210-byte super-blocks (128 bytes of low nibbles ql, 64 of high bit
+// pairs qh, 16 int8 scales, fp16 d); element e's code is the nibble of
+// ql[64 h + 32 (i % 2) + l] at 4 (i / 2) with the bit pair of qh[32 h + l] at
+// 2 i above it (h = e / 128, i = e % 128 / 32, l = e % 32), and its weight
+// d scale[e / 16] (q - 32), exact in fp32 (11 + 7 + 6 significant bits).
+// A lane group's 8 positions of a unit lie in one scale's run of 16 and read
+// 8 consecutive bytes of ql and of qh.  210-byte blocks are no whole number
+// of granules per chunk, so Q6_K takes the register kernel.
+template <> struct MfmaFmt<QG_Q6_K> {
+  static constexpr int kBytes = 210, kCB = 0;
+  struct Raw { uint2 ql, qh; float dsc; uint32_t shl, shh; };
+  __device__ static inline int x0(int g) { return 8 * g; }
+  __device__ static inline int x1(int g) { return 8 * g + 4; }
+  __device__ static inline Raw load_unit(const uint8_t *row, int u, int g) {
+    const uint8_t *sb = row + (int64_t)(u >> 3) * 210;
+    const int uu = u & 7, h = uu >> 2, i = uu & 3;
+    Raw r;
+    __builtin_memcpy(&r.ql, sb + 64 * h + 32 * (i & 1) + 8 * g, 8);
+    __builtin_memcpy(&r.qh, sb + 128 + 32 * h + 8 * g, 8);
+    uint16_t hd;
+    __builtin_memcpy(&hd, sb + 208, 2);
+    r.dsc = __half2float(__ushort_as_half(hd)) * (float)(int8_t)sb[192 + 2 * uu + (g >> 1)];
+    r.shl = 4u * (uint32_t)(i >> 1);
+    r.shh = 2u * (uint32_t)i;
+    return r;
+  }
+  __device__ static inline float scale(const Raw &r) { return r.dsc; }
+  template <int S> __device__ static inline float w(const Raw &r, float dsc) {
+    const uint32_t lo = ((S < 4 ? r.ql.x : r.ql.y) >> (8 * (S & 3) + r.shl)) & 15u;
+    const uint32_t hi = ((S < 4 ? r.qh.x : r.qh.y) >> (8 * (S & 3) + r.shh)) & 3u;
+    return dsc * (float)((int)(lo | (hi << 4)) - 32);
+  }
+};
+
 template <int FMT, int S, int RT>
 __device__ __forceinline__ void mfma_steps(const typename MfmaFmt<FMT>::Raw (&r)[RT], const float (&sc)[RT],
                                            const float (&xv)[8], f32x4 (&acc)[RT]) {
@@ -194,7 +228,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_mfma_kernel(const MfmaArgs a) {
         __builtin_memcpy(&v[p], xp + 32 * bb + xo1, 16);
       }
 #pragma unroll
-      for (int t = 0; t < RT; ++t) r[p][t] = F::load(rowp[t] + (int64_t)bb * F::kBytes, g);
+      for (int t = 0; t < RT; ++t) r[p][t] = F::load_unit(rowp[t], bb, g);
     }
   };
   const int rounds = (nb + WT - 1) / WT;  // blocks per wave, rounded up
@@ -388,16 +422,20 @@ __global__ void __launch_bounds__(64 * WT) gemv_mfma_lds_kernel(const MfmaArgs a
 // Launch shape: two 16-row tiles per workgroup (each x value loaded once for
 // 32 rows) and 8 waves; of the shapes measured on the 20B-class pass (1-2
 // tiles, 4-16 waves, with and without LDS staging) the fastest.  A matrix
-// shorter than one chunk (k < 32 kCB) takes the register kernel.
+// shorter than one chunk (k < 32 kCB), and Q6_K, take the register kernel.
 template <int FMT>
 static int launch_fmt(const MfmaArgs &a, hipStream_t stream) {
   constexpr int RT = 2, WT = 8;
   const int64_t tiles = (a.n_rows + 16 * RT - 1) / (16 * RT);
   if (tiles > 0x7fffffff) return QG_E_SHAPE;
-  if (a.nb >= MfmaFmt<FMT>::kCB) {
-    hipLaunchKernelGGL((gemv_mfma_lds_kernel<FMT, RT, WT>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
-  } else if constexpr (FMT != QG_Q4_K) {  // (a Q4_K row is at least one chunk)
+  if constexpr (FMT == QG_Q6_K) {
     hipLaunchKernelGGL((gemv_mfma_kernel<FMT, RT, WT, 2>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
+  } else {
+    if (a.nb >= MfmaFmt<FMT>::kCB) {
+      hipLaunchKernelGGL((gemv_mfma_lds_kernel<FMT, RT, WT>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
+    } else if constexpr (FMT != QG_Q4_K) {  // (a Q4_K row is at least one chunk)
+      hipLaunchKernelGGL((gemv_mfma_kernel<FMT, RT, WT, 2>), dim3((unsigned)tiles), dim3(64 * WT), 0, stream, a);
+    }
   }
   return QG_OK;
 }
@@ -408,6 +446,7 @@ int launch_gemv_mfma(int32_t fmt, const MfmaArgs &a, hipStream_t stream) {
     case QG_Q4_0: return launch_fmt<QG_Q4_0>(a, stream);
     case QG_MXFP4: return launch_fmt<QG_MXFP4>(a, stream);
     case QG_Q4_K: return launch_fmt<QG_Q4_K>(a, stream);
+    case QG_Q6_K: return launch_fmt<QG_Q6_K>(a, stream);
     default: return QG_E_FMT;
   }
 }

@@ -1083,7 +1083,6 @@ int qgemv_rows_mfma(const qg_matrix *w, int64_t row_start, int64_t row_end, cons
   if (rc) return rc;
   if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
   const int64_t n = row_end - row_start;
-  if (w->fmt != QG_Q8_0 && w->fmt != QG_Q4_0 && w->fmt != QG_MXFP4 && w->fmt != QG_Q4_K) return QG_E_FMT;
   if (n_tok < 0 || x_stride < 0 || (n_tok > 1 && y_stride < n)) return QG_E_ARG;
   if (n == 0 || n_tok == 0) return QG_OK;
   if (!x || !y) return QG_E_NULL;
@@ -1094,7 +1093,7 @@ int qgemv_rows_mfma(const qg_matrix *w, int64_t row_start, int64_t row_end, cons
   a.n_rows = n;
   a.x_stride = x_stride;
   a.y_stride = y_stride;
-  a.nb = (int32_t)(w->k / 32);  // 32-weight units (a Q4_K super-block is 8)
+  a.nb = (int32_t)(w->k / 32);  // 32-weight units (a K-quant super-block is 8)
   // passes of 16 tokens, each reading the weights once
   for (int32_t t = 0; t < n_tok; t += 16) {
     a.x = x + (int64_t)t * x_stride;

@@ -34,10 +34,12 @@ def sync():
 # kernel with one chunk (Q8_0 k = 256), whole chunks, and a last chunk moved
 # back over its predecessor (Q8_0 and Q4_0 k = 2080, MXFP4 k = 2880); the
 # register kernel below one chunk (Q8_0 k = 96, Q4_0 k = 480, MXFP4 k = 32);
-# Q4_K with one, 24 and 11 super-blocks per row
+# Q4_K with one, 24 and 11 super-blocks per row; Q6_K (register kernel) with
+# 96, one and 11
 SHAPES = [(q.Q8_0, 300, 6144), (q.Q8_0, 17, 24576), (q.Q8_0, 64, 256), (q.Q8_0, 50, 2080), (q.Q8_0, 5, 96),
           (q.Q4_0, 257, 4096), (q.Q4_0, 33, 2080), (q.Q4_0, 20, 480), (q.MXFP4, 200, 2880), (q.MXFP4, 16, 32),
-          (q.Q4_K, 130, 6144), (q.Q4_K, 33, 256), (q.Q4_K, 70, 2816)]
+          (q.Q4_K, 130, 6144), (q.Q4_K, 33, 256), (q.Q4_K, 70, 2816),
+          (q.Q6_K, 71, 24576), (q.Q6_K, 40, 256), (q.Q6_K, 33, 2816)]
 
 
 def oracle_tokens(fmt, w, rows, k, xs):
@@ -153,10 +155,6 @@ def test_mfma_noops_and_errors(dev):
     q.qgemv_rows_mfma(M, 0, rows, x[:0], y[:0])      # no tokens
     sync()
     assert np.all(y.cpu().numpy() == 7.0)
-    wk = synth.blocks(q.Q6_K, 4, 256, synth.seed_of(31, 61))
-    MK = q.Matrix(dput(wk, dev), q.Q6_K, 4, 256)
-    with pytest.raises(q.QgemvError):
-        q.qgemv_rows_mfma(MK, 0, 4, x, y)
     y2 = torch.empty((2, rows + 1), dtype=torch.float32, device=dev)
     with pytest.raises(q.QgemvError):
         q.qgemv_rows_mfma(M, 0, rows + 1, x, y2)
