@@ -86,6 +86,13 @@ __global__ void dequant_kernel(const uint8_t *base, int64_t row_start, int64_t n
 #pragma unroll
     for (int e = 0; e < 32; ++e) o[e] = w[e];
     return;
+  } else if constexpr (F::kDot) {
+    float w[32];
+    F::dequant(base + (row_start + r) * row_bytes + (int64_t)F::kBytes * j, w);
+    float *o = out + r * (int64_t)nb * 32 + 32 * j;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[e] = w[e];
+    return;
   } else {
   const uint8_t *p = base + (row_start + r) * row_bytes + (int64_t)F::kBytes * j;
   uint32_t sbits = 0, q[F::kWords];

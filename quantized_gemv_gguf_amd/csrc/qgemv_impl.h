@@ -27,13 +27,14 @@ constexpr int kMaxWT = 12;       // waves per team
 // ---------------------------------------------------------------------------
 // Formats.  The unit of work of a lane is 32 consecutive weights: a whole
 // block of the 32-weight formats, one sub-block (kUnits = 8 per block) of the
-// 256-weight K-quant super-blocks.  A 32-weight block is a scale field
-// followed by a payload of kWords 32-bit words.  decode() turns the payload
-// into 32 "unit" values u_j and scale() the scale field into a Scale such that
-// the weight is w_j = apply(scale, u_j); the GEMV applies the scale once to a
-// block's partial dot product, the dequant kernel applies it to every u_j.
-// Both use the same decoder, so the bit-exact decode check covers the GEMV's
-// decoder.
+// 256-weight K-quant super-blocks.  Q8_0 and MXFP4: decode() turns a block's
+// payload into 32 "unit" values u_j and scale() its scale field into a Scale
+// with w_j = apply(scale, u_j); the GEMV applies the scale once to a block's
+// partial dot product, the dequant kernel to every u_j.  Q4_0 and the
+// K-quants (kDot) have a dot() of their own and a dequant() built from the
+// same code formation.  The bit-exact decode check therefore covers the code
+// formation of every format's GEMV; the one-hot GEMV tests (x a unit vector,
+// every position of a block) cover the GEMV's own arithmetic on it.
 // ---------------------------------------------------------------------------
 
 template <int FMT> struct Fmt;
@@ -59,41 +60,49 @@ template <> struct Fmt<QG_Q8_0> {
 
 // Q4_0: fp16 d, 16 bytes of nibbles; w = d * (q - 8) (RAMforge README,
 // "Milestone 5").  Element j < 16 is the low nibble of byte j, element j + 16
-// the high nibble.  Decode (the dequant kernel): (q ^ 8) is q - 8 in 4-bit
-// two's complement; moved to the top of a byte it reads as the int8
-// 16 * (q - 8), exactly, and the 1/16 goes into the scale (a power of two, so
-// d/16 is exact too).  Dot (the GEMV): two codes per word become fp16
-// subnormals q 2^-24 that v_fma_mix_f32 multiplies into the fp32 sums with no
-// conversion instruction (7 bit operations and 8 FMAs per 8 weights, against
-// 3 + 8 conversions + 8 FMAs), and the offset comes out as
-// d (2^24 sum q x - 8 sum x), with sum x per block formed once per
-// activation vector.
+// the high nibble.  Every code is turned into its weight's exact code value
+// before it meets x, so a weight of zero adds exactly zero and a row of zero
+// weights gives exactly 0.  Two codes at a time: a nibble masked into the
+// mantissa of the fp16 1024 (0x6400) gives 1024 + q (a high nibble, masked in
+// place, gives 1024 + 16 q), and one packed fp16 subtraction of 1032 (1152)
+// leaves q - 8 (16 (q - 8)) exactly; v_fma_mix_f32 takes those fp16 values
+// straight into the fp32 FMAs.  That is 1 shift, 4 and-or, 4 packed
+// subtractions and 8 FMAs per 8 weights; the high nibbles' factor 16 comes
+// out once per block, exactly.  The dequant kernel forms the weights from the
+// same codes().
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 template <> struct Fmt<QG_Q4_0> {
   static constexpr int kBytes = 18, kScaleBytes = 2, kWords = 4, kUnits = 1;
-  static constexpr bool kSums = true, kDot = true;
-  struct Scale { float d16; };
-  __device__ static inline Scale scale(uint32_t bits) {
-    return Scale{__half2float(__ushort_as_half((uint16_t)bits)) * 0.0625f};
-  }
-  __device__ static inline void decode(const uint32_t *q, float u[32]) {
+  static constexpr bool kSums = false, kDot = true;
+  // Word i of the payload (bytes 4i .. 4i+3) gives four fp16 pairs:
+  //   lo[2i]     = (q_{4i}      - 8,  q_{4i+2}      - 8)   low nibbles of bytes 0, 2
+  //   lo[2i + 1] = (q_{4i+1}    - 8,  q_{4i+3}      - 8)   low nibbles of bytes 1, 3
+  //   hi[2i]     = 16 (q_{16+4i}   - 8, q_{16+4i+2} - 8)   high nibbles of bytes 0, 2
+  //   hi[2i + 1] = 16 (q_{16+4i+1} - 8, q_{16+4i+3} - 8)   high nibbles of bytes 1, 3
+  __device__ static inline void codes(const uint32_t (&q)[4], h16x2 (&lo)[8], h16x2 (&hi)[8]) {
+    const h16x2 b_lo = {(_Float16)1032.0f, (_Float16)1032.0f}, b_hi = {(_Float16)1152.0f, (_Float16)1152.0f};
+    // The exponent bits in a register the compiler cannot fold, so that each
+    // mask-and-insert is one v_and_or_b32 (mask from a scalar register)
+    // rather than an and and an or with literals.
+    uint32_t e = 0x64006400u;
+    asm("" : "+v"(e));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t v = q[i] ^ 0x88888888u;
-      const uint32_t hi = v & 0xF0F0F0F0u;
-      const uint32_t lo = (v << 4) & 0xF0F0F0F0u;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        u[4 * i + k] = (float)(int8_t)(lo >> (8 * k));
-        u[16 + 4 * i + k] = (float)(int8_t)(hi >> (8 * k));
-      }
+      const uint32_t w = q[i], v = q[i] >> 8;
+      lo[2 * i] = __builtin_bit_cast(h16x2, (w & 0x000F000Fu) | e) - b_lo;
+      lo[2 * i + 1] = __builtin_bit_cast(h16x2, (v & 0x000F000Fu) | e) - b_lo;
+      hi[2 * i] = __builtin_bit_cast(h16x2, (w & 0x00F000F0u) | e) - b_hi;
+      hi[2 * i + 1] = __builtin_bit_cast(h16x2, (v & 0x00F000F0u) | e) - b_hi;
     }
   }
-  __device__ static inline float apply(Scale s, float v) { return s.d16 * v; }
-  __device__ static inline float fma_acc(Scale s, float v, float acc) { return fmaf(s.d16, v, acc); }
-  // res[t] = acc[t] + the block's dot with token t's inputs.
+  // res[t] = acc[t] + the block's dot with token t's inputs: the low-nibble
+  // elements in chains p0 (elements 4i, 4i + 2) and p1 (4i + 1, 4i + 3), the
+  // high ones (times 16) in p2 and p3; then d ((p0 + p1) + (p2 + p3) / 16).
   template <int NT>
   __device__ static inline void dot(const uint8_t *blk, const float (&x)[NT][32], const float (&xs)[NT][2],
                                     const float (&acc)[NT], float (&res)[NT]);
+  // The 32 weights, from the same codes as the dot: d (q - 8), exact in fp32.
+  __device__ static inline void dequant(const uint8_t *blk, float w[32]);
 };
 
 // MXFP4: E8M0 e, 16 bytes of E2M1 nibbles; w = 2^(e-127) * E2M1(nib) (block
@@ -135,31 +144,49 @@ __device__ __forceinline__ float h16_hi(uint32_t v) {
 }
 
 template <int NT>
-__device__ inline void Fmt<QG_Q4_0>::dot(const uint8_t *blk, const float (&x)[NT][32], const float (&xs)[NT][2],
+__device__ inline void Fmt<QG_Q4_0>::dot(const uint8_t *blk, const float (&x)[NT][32], const float (&)[NT][2],
                                          const float (&acc)[NT], float (&res)[NT]) {
   uint32_t sbits = 0, q[4];
   __builtin_memcpy(&sbits, blk, 2);
   __builtin_memcpy(q, blk + 2, 16);
   const float d = half_bits(sbits);
+  h16x2 lo[8], hi[8];
+  codes(q, lo, hi);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // word i: low nibbles are elements 4i..4i+3, high nibbles 16+4i..16+4i+3
-      const uint32_t a = q[i] & 0x000F000Fu, b = (q[i] >> 8) & 0x000F000Fu;
-      const uint32_t c = (q[i] >> 4) & 0x000F000Fu, e = (q[i] >> 12) & 0x000F000Fu;
-      p[0] = fmaf(h16_lo(a), x[t][4 * i + 0], p[0]);
-      p[1] = fmaf(h16_lo(b), x[t][4 * i + 1], p[1]);
-      p[2] = fmaf(h16_hi(a), x[t][4 * i + 2], p[2]);
-      p[3] = fmaf(h16_hi(b), x[t][4 * i + 3], p[3]);
-      p[0] = fmaf(h16_lo(c), x[t][16 + 4 * i + 0], p[0]);
-      p[1] = fmaf(h16_lo(e), x[t][16 + 4 * i + 1], p[1]);
-      p[2] = fmaf(h16_hi(c), x[t][16 + 4 * i + 2], p[2]);
-      p[3] = fmaf(h16_hi(e), x[t][16 + 4 * i + 3], p[3]);
+      p[0] = fmaf((float)lo[2 * i][0], x[t][4 * i + 0], p[0]);
+      p[1] = fmaf((float)lo[2 * i + 1][0], x[t][4 * i + 1], p[1]);
+      p[2] = fmaf((float)hi[2 * i][0], x[t][16 + 4 * i + 0], p[2]);
+      p[3] = fmaf((float)hi[2 * i + 1][0], x[t][16 + 4 * i + 1], p[3]);
+      p[0] = fmaf((float)lo[2 * i][1], x[t][4 * i + 2], p[0]);
+      p[1] = fmaf((float)lo[2 * i + 1][1], x[t][4 * i + 3], p[1]);
+      p[2] = fmaf((float)hi[2 * i][1], x[t][16 + 4 * i + 2], p[2]);
+      p[3] = fmaf((float)hi[2 * i + 1][1], x[t][16 + 4 * i + 3], p[3]);
     }
-    const float r = fmaf(d * 0x1p24f, (p[0] + p[1]) + (p[2] + p[3]), acc[t]);
-    res[t] = fmaf(-8.0f * d, xs[t][0] + xs[t][1], r);
+    res[t] = fmaf(d, fmaf(p[2] + p[3], 0.0625f, p[0] + p[1]), acc[t]);
+  }
+}
+
+__device__ inline void Fmt<QG_Q4_0>::dequant(const uint8_t *blk, float w[32]) {
+  uint32_t sbits = 0, q[4];
+  __builtin_memcpy(&sbits, blk, 2);
+  __builtin_memcpy(q, blk + 2, 16);
+  const float d = half_bits(sbits);
+  h16x2 lo[8], hi[8];
+  codes(q, lo, hi);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[4 * i + 0] = d * (float)lo[2 * i][0];
+    w[4 * i + 1] = d * (float)lo[2 * i + 1][0];
+    w[4 * i + 2] = d * (float)lo[2 * i][1];
+    w[4 * i + 3] = d * (float)lo[2 * i + 1][1];
+    w[16 + 4 * i + 0] = d * ((float)hi[2 * i][0] * 0.0625f);
+    w[16 + 4 * i + 1] = d * ((float)hi[2 * i + 1][0] * 0.0625f);
+    w[16 + 4 * i + 2] = d * ((float)hi[2 * i][1] * 0.0625f);
+    w[16 + 4 * i + 3] = d * ((float)hi[2 * i + 1][1] * 0.0625f);
   }
 }
 
@@ -249,27 +276,34 @@ template <> struct Fmt<QG_Q4_K> {
 // d; w = d scale (q - 32) (GGUF's layout; the pages name the format only).
 // Unit u = 4 h + i (32 weights 128 h + 32 i + l) takes its low nibbles from
 // ql[64 h + 32 (i & 1) + l] (high nibble for i >= 2), its top bits from bits
-// 2 i, 2 i + 1 of qh[32 h + l], its scales from bytes 2 u, 2 u + 1.  A unit's
-// dot is d (scale_a (sum q x - 32 sum x) + scale_b (...)) over its halves,
-// with the half sums of x formed once per activation vector.
+// 2 i, 2 i + 1 of qh[32 h + l], its scales from bytes 2 u, 2 u + 1.  Each
+// 6-bit code is formed as the int8 4 (q - 32), exactly: its low four bits
+// rotated to bits 2..5 of the byte, the top two to bits 6, 7 with the top one
+// flipped (q ^ 32 is q - 32 in 6-bit two's complement), so a weight of zero
+// (q = 32) adds exactly zero and the dot takes no sum of x.  The factor 4
+// comes out of d exactly.  The dequant kernel forms the weights from the same
+// codes().
 template <> struct Fmt<QG_Q6_K> {
   static constexpr int kBytes = 210, kUnits = 8;
-  static constexpr bool kSums = true, kDot = true;
+  static constexpr bool kSums = false, kDot = true;
+  // Byte l of word w of q is 4 (q_e - 32) for element e = 4 w + l of unit u.
   template <typename P>
   __device__ static inline void codes(const P *blk, int u, uint32_t q[8]) {
     const int h = u >> 2, i = u & 3;
     uint32_t lo[8], hi[8];
     __builtin_memcpy(lo, blk + 64 * h + 32 * (i & 1), 32);
     __builtin_memcpy(hi, blk + 128 + 32 * h, 32);
-    // bits 2 i, 2 i + 1 of each high byte move to bits 4, 5 by one rotation
-    // (bits that wrap into another byte land outside the kept field)
-    const int s4 = 4 * (i >> 1), rot = (2 * i - 4) & 31;
+    // rotations right: the nibble at bit 4 (i >= 2) or 0 of each byte to bit
+    // 2; bits 2 i, 2 i + 1 to bits 6, 7 (bits that wrap into another byte land
+    // outside the kept field)
+    const int rlo = (i >> 1) ? 2 : 30, rhi = (2 * i - 6) & 31;
 #pragma unroll
     for (int w = 0; w < 8; ++w)
-      q[w] = ((lo[w] >> s4) & 0x0F0F0F0Fu) | (__builtin_amdgcn_alignbit(hi[w], hi[w], rot) & 0x30303030u);
+      q[w] = ((__builtin_amdgcn_alignbit(lo[w], lo[w], rlo) & 0x3C3C3C3Cu) |
+              (__builtin_amdgcn_alignbit(hi[w], hi[w], rhi) & 0xC0C0C0C0u)) ^ 0x80808080u;
   }
   template <int NT>
-  __device__ static inline void dot(const uint8_t *blk, int u, const float (&x)[NT][32], const float (&xs)[NT][2],
+  __device__ static inline void dot(const uint8_t *blk, int u, const float (&x)[NT][32], const float (&)[NT][2],
                                     const float (&acc)[NT], float (&res)[NT]) {
     uint32_t q[8];
     codes(blk, u, q);
@@ -284,9 +318,8 @@ template <> struct Fmt<QG_Q6_K> {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           p[2 * (w >> 2) + (k & 1)] =
-              fmaf((float)((q[w] >> (8 * k)) & 0xffu), x[t][4 * w + k], p[2 * (w >> 2) + (k & 1)]);
-      const float pa = fmaf(-32.0f, xs[t][0], p[0] + p[1]), pb = fmaf(-32.0f, xs[t][1], p[2] + p[3]);
-      res[t] = fmaf(half_bits(hd), fmaf(sa, pa, sb * pb), acc[t]);
+              fmaf((float)(int8_t)(q[w] >> (8 * k)), x[t][4 * w + k], p[2 * (w >> 2) + (k & 1)]);
+      res[t] = fmaf(half_bits(hd) * 0.25f, fmaf(sa, p[0] + p[1], sb * (p[2] + p[3])), acc[t]);
     }
   }
   // The 32 weights of unit u, each rounded once: d scale is exact in fp32.
@@ -295,13 +328,12 @@ template <> struct Fmt<QG_Q6_K> {
     codes(blk, u, q);
     uint32_t hd = 0;
     __builtin_memcpy(&hd, blk + 208, 2);
-    const float d = half_bits(hd);
-    const float da = d * (float)(int8_t)blk[192 + 2 * u], db = d * (float)(int8_t)blk[193 + 2 * u];
+    const float d4 = half_bits(hd) * 0.25f;
+    const float da = d4 * (float)(int8_t)blk[192 + 2 * u], db = d4 * (float)(int8_t)blk[193 + 2 * u];
 #pragma unroll
     for (int v = 0; v < 8; ++v)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[4 * v + k] = (v < 4 ? da : db) * (float)((int)((q[v] >> (8 * k)) & 0xffu) - 32);
+      for (int k = 0; k < 4; ++k) w[4 * v + k] = (v < 4 ? da : db) * (float)(int8_t)(q[v] >> (8 * k));
   }
 };
 

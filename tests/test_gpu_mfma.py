@@ -108,9 +108,10 @@ def test_mfma_matches_batch_within_gates(dev):
 
 
 def test_mfma_special_values(dev):
-    """NaN scales (MXFP4 e = 255) make exactly their rows NaN; Q8_0 zero-scale
-    rows give exact zeros; the largest fp16 scale stays finite and within the
-    gates."""
+    """NaN scales (MXFP4 e = 255) make exactly their rows NaN; rows of
+    fp32-subnormal weights (e = 0) pass the gates like any other; Q8_0
+    zero-scale rows give exact zeros; the largest fp16 scale stays finite and
+    within the gates."""
     import torch
     k = 512
     w = synth.blocks(q.MXFP4, 48, k, synth.seed_of(31, 50)).reshape(48, -1)
@@ -125,10 +126,11 @@ def test_mfma_special_values(dev):
     assert np.all(np.isnan(got[:, 5]))
     assert np.all(np.isfinite(np.delete(got, 5, axis=1)))
     ref, a = oracle_tokens(q.MXFP4, w.reshape(-1), 48, k, xs)
-    # (row 20's weights are fp32 subnormals; only finiteness is asked of it)
-    keep = [r for r in range(48) if r not in (5, 20)]
+    keep = [r for r in range(48) if r != 5]
     for t in range(4):
         check(got[t, keep], ref[t, keep], a[t, keep], what=f"token {t}")
+        # row 20: fp32-subnormal weights, which the matrix cores must not flush
+        check(got[t, 20:21], ref[t, 20:21], a[t, 20:21], what=f"subnormal row, token {t}")
 
     w8 = synth.blocks(q.Q8_0, 32, k, synth.seed_of(31, 51)).reshape(32, -1)
     w8[3, 0::34] = 0; w8[3, 1::34] = 0          # row 3: d = 0
