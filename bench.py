@@ -79,17 +79,72 @@ def profiled_traffic(kernel: str):
 
 
 def threads() -> int:
-    return int(os.environ.get("OMP_NUM_THREADS", 0) or min(16, os.cpu_count() or 1))
+    """Host threads for the oracle and the generators: every CPU this process
+    may run on, capped by OMP_NUM_THREADS where the host sets it (a GPU machine
+    gives each GPU a share of its cores that way)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = int(os.environ.get("OMP_NUM_THREADS", 0) or 0)
+    return max(1, min(n, cap) if cap > 0 else n)
 
 
 def cpu_model() -> str:
+    """The CPU's full model string, with its family/model/stepping numbers."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = [t.strip() for t in line.split(":", 1)]
+                info.setdefault(k, v)
     except OSError:
         pass
-    return platform.processor() or "unknown"
+    name = info.get("model name") or platform.processor() or "unknown"
+    extra = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({extra})" if extra else name
+
+
+def host_info() -> dict:
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": aff,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def sha256_of(t) -> str:
+    """SHA-256 of a tensor's bytes (I4: output hashes compared across runs)."""
+    import hashlib
+    a = t.detach().contiguous().cpu().numpy()
+    return hashlib.sha256(a.tobytes()).hexdigest()
+
+
+def read_ceiling(dev, nbytes=4 << 30, reps=9):
+    """The same run's plain streaming-read rate (qgemv_read_ceiling over 4 GiB,
+    far above the 256 MB MALL): median of `reps` reads, HIP events around each."""
+    import torch
+    import quantized_gemv_gguf_amd as q
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        q.qgemv_read_ceiling(buf, sink)
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        q.qgemv_read_ceiling(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = float(np.median(ms))
+    del buf
+    torch.cuda.empty_cache()
+    gbs = nbytes / (med / 1e3) / 1e9
+    return {"GBs": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS, "bytes_per_read": nbytes,
+            "ms_per_read_median": med, "reads": reps,
+            "kernel": "qgemv_read_ceiling: 2048 x 256 lanes, one 16-byte non-temporal load per lane per step"}
 
 
 # --- the dense decode pass -------------------------------------------------------
@@ -284,6 +339,10 @@ def dense_workload(args, dev, cfg=5):
         for _ in range(max(args.warmup, 1)):
             graph.replay()
         torch.cuda.synchronize()
+    # the carry entering the first timed token: the timed tokens are replayed
+    # from it afterwards for the parity check (I4: the replay must give the
+    # timed run's bits)
+    d_start = model.d.clone()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -297,6 +356,7 @@ def dense_workload(args, dev, cfg=5):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = g0.elapsed_time(g1)
+    d_end = model.d.clone()
     # per-kernel durations: right after the timed region, each kernel variant's
     # launches of two tokens run back to back on the launch stream, bracketed by
     # one pair of HIP events (an event pair around every single launch would
@@ -337,14 +397,78 @@ def dense_workload(args, dev, cfg=5):
                      "traffic": profiled_traffic(dom_k), "avg_launch_us": ms / cnt * 1e3,
                      "bytes_per_launch": b / cnt},
         "kernels": kernels,
+        "sha256_final_carry": sha256_of(d_end),
     }
     # identity: tokens/s = bandwidth / active bytes per token
     assert abs(res["tokens_per_s"] - gbs * 1e9 / model.bytes_per_token) <= 1e-9 * res["tokens_per_s"]
     if not args.no_check:
-        res["parity"] = dense_parity(model, layers)
+        res["parity"] = dense_replay_parity(model, layers, d_start, d_end, args.steps,
+                                            free_running=not args.no_free_running)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = dense_cpu_baseline(model, args.cpu_seconds)
+        res["cpu_baseline"] = dense_cpu_baselines(model, args.cpu_seconds)
+    del model
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return res
+
+
+def dense_replay_parity(model, layers, d_start, d_end, steps, free_running=True):
+    """Parity of the timed tokens.  They are replayed from the carry that
+    entered the first one; the replay must end on the timed run's bits (I4),
+    so checking it checks them.  On the first and the last timed token every
+    one of the 176 GEMVs is teacher-forced (dense_parity); the free-running
+    oracle (its own fp64 sums from the same starting carry, inputs rounded to
+    fp32 per step) is reported for the first token, not gated."""
+    import torch
+    model.d.copy_(d_start)
+    forced = {}
+    d_after0 = None
+    for t in range(steps):
+        if t in (0, steps - 1):
+            forced[t] = dense_parity(model, layers, seed=7 + t, every_gemv=True)
+        else:
+            model.token_fused()
+        if t == 0:
+            torch.cuda.synchronize()
+            d_after0 = model.d.cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(model.d.view(torch.int32), d_end.view(torch.int32)))
+    worst_c = max(v["max_componentwise"] for v in forced.values())
+    worst_n = max(v["max_normwise_sampled"] for v in forced.values())
+    out = {"teacher_forced": {"tokens": sorted({0, steps - 1}), "gemvs_per_token": len(model.fcalls),
+                              "rows_checked": sum(v["rows_checked"] for v in forced.values()),
+                              "max_componentwise": worst_c, "max_normwise_sampled": worst_n},
+           "replay_bit_identical_to_timed_run": same, "tol": TOL,
+           "pass": bool(same and worst_c <= TOL and worst_n <= TOL)}
+    if free_running:
+        out["free_running_token0"] = dense_free_running(model, d_start.cpu().numpy(), d_after0)
+    return out
+
+
+def dense_free_running(model, d_in, d_gpu):
+    """The oracle's own pass of one token from the GPU's starting carry (every
+    row of every GEMV, fp64 sums; each step's input rounded to fp32 as the
+    oracle takes it): the normwise difference of the final carry from the
+    GPU's.  Errors compound over 176 steps, so this is reported, not gated."""
+    import oracle
+    nth = threads()
+    t = time.perf_counter()
+    c = oracle.rms_carry(d_in.astype(np.float64), model.eps)
+    for l in range(model.L):
+        fm = model.fmts
+        ws = [synth.blocks(fm[m], r, k, model.seed(l, m), threads=nth) for m, (_, r, k) in enumerate(model.shapes)]
+        y, _ = oracle.gemv_rows(fm[0], ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
+        c = oracle.rms_carry(y[2 * model.H:3 * model.H], model.eps)
+        y, _ = oracle.gemv_rows(fm[1], ws[1], *model.shapes[1][1:], c.astype(np.float32), threads=nth)
+        c = oracle.rms_carry(y, model.eps)
+        y, _ = oracle.gemv_rows(fm[2], ws[2], *model.shapes[2][1:], c.astype(np.float32), threads=nth)
+        act = oracle.rms_carry(y, model.eps, gelu=True)
+        y, _ = oracle.gemv_rows(fm[3], ws[3], *model.shapes[3][1:], act.astype(np.float32), threads=nth)
+        c = y  # the raw down output is the carry the next token's first GEMV normalises
+    err = np.abs(d_gpu - c)
+    return {"max_abs_diff_over_max_abs": float(err.max() / np.abs(c).max()),
+            "mean_abs_diff_over_mean_abs": float(err.mean() / np.abs(c).mean()),
+            "seconds": round(time.perf_counter() - t, 1), "gated": False}
 
 
 def dense_chain_workload(args, dev, model, c, layers):
@@ -395,7 +519,7 @@ def dense_chain_workload(args, dev, model, c, layers):
     if not args.no_check:
         res["parity"] = dense_chain_parity(model, layers)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = dense_cpu_baseline(model, args.cpu_seconds)
+        res["cpu_baseline"] = dense_cpu_baselines(model, args.cpu_seconds)
     model.chain.close()
     torch.cuda.synchronize()
     return res
@@ -433,14 +557,18 @@ def dense_chain_parity(model, layers, n_rows=48, seed=7):
             "tol": TOL, "pass": bool(ok), "teacher_forced": "fp64 rms of the GPU's own step inputs"}
 
 
-def dense_parity(model, layers, n_rows=48, seed=7):
-    """Teacher-forced check of sampled rows of every GEMV of layers 0 and
-    layers-1 (their inputs and outputs copied back), against the oracle on
-    weight rows regenerated on the host."""
+def dense_parity(model, layers, n_rows=48, seed=7, every_gemv=False):
+    """Teacher-forced check of one token's GEMVs (every GEMV, or those of
+    layers 0 and layers-1): each one's input is copied back, the oracle
+    normalises it in fp64 and multiplies sampled rows (8 runs of n_rows/8
+    consecutive rows, so tile edges are crossed) regenerated on the host."""
     import torch
     import oracle
     rng = np.random.default_rng(seed)
-    want = {0, 1, 2, 3, 4 * (layers - 1), 4 * (layers - 1) + 1, 4 * (layers - 1) + 2, 4 * (layers - 1) + 3}
+    if every_gemv:
+        want = set(range(len(model.fcalls)))
+    else:
+        want = {0, 1, 2, 3, 4 * (layers - 1), 4 * (layers - 1) + 1, 4 * (layers - 1) + 2, 4 * (layers - 1) + 3}
     # fused launches: GEMV i normalises its raw input (oracle: fp64 RMS of
     # the GPU's own input) and the up projection stores gelu(u)
     outs = [model.qkv, model.o, model.a, model.d]
@@ -448,6 +576,7 @@ def dense_parity(model, layers, n_rows=48, seed=7):
     checked = 0
     H = model.H
     state = {}
+    run = max(1, n_rows // 8)
 
     def raw_input(i, m):
         if m == 0:
@@ -469,12 +598,14 @@ def dense_parity(model, layers, n_rows=48, seed=7):
         if m == 3:
             state["d_in"] = model.d.cpu().numpy()
         _, r, k = model.shapes[m]
-        rows = np.sort(rng.choice(r, n_rows, replace=False))
-        ref, a = np.empty(n_rows), np.empty(n_rows)
-        for j, row in enumerate(rows):
-            f = model.fmts[m]
-            wrow = synth.blocks(f, r, k, model.seed(i // 4, m), r0=int(row), r1=int(row) + 1, threads=1)
-            ref[j], a[j] = [v[0] for v in oracle.gemv_rows(f, wrow, 1, k, x, threads=1)]
+        f = model.fmts[m]
+        starts = np.sort(rng.choice(r // run, 8, replace=False)) * run
+        rows = np.concatenate([np.arange(s0, s0 + run) for s0 in starts])
+        ref, a = np.empty(rows.size), np.empty(rows.size)
+        for j, s0 in enumerate(starts):
+            w = synth.blocks(f, r, k, model.seed(i // 4, m), r0=int(s0), r1=int(s0) + run, threads=1)
+            rr, aa = oracle.gemv_rows(f, w, run, k, x, threads=1)
+            ref[j * run:(j + 1) * run], a[j * run:(j + 1) * run] = rr, aa
         if m == 2:  # the stored output is gelu(u): compare u's GELU in fp64
             from math import erfc, sqrt
             ref = np.array([0.5 * v * erfc(-v / sqrt(2.0)) for v in ref])
@@ -488,32 +619,42 @@ def dense_parity(model, layers, n_rows=48, seed=7):
         # a degenerate sample (all-zero or non-finite rows) fails the check
         worst_c = max(worst_c, c_ if np.isfinite(c_) else np.inf)
         worst_n = max(worst_n, n_ if np.isfinite(n_) else np.inf)
-        checked += n_rows
+        checked += rows.size
 
     torch.cuda.synchronize()
     state["d_in"] = model.d.cpu().numpy()
     model.token_fused(hook=hook)
     torch.cuda.synchronize()
     ok = worst_c <= TOL and worst_n <= TOL
-    return {"rows_checked": checked, "max_componentwise": worst_c, "max_normwise_sampled": worst_n,
-            "tol": TOL, "pass": bool(ok)}
+    return {"rows_checked": checked, "gemvs_checked": len(want), "max_componentwise": worst_c,
+            "max_normwise_sampled": worst_n, "tol": TOL, "pass": bool(ok)}
 
 
-def dense_cpu_baseline(model, seconds):
-    """The oracle (fp64, all threads) on the same pass: token after token,
-    layer by layer from token 0's carry, until `seconds` of oracle time have
-    run (weight regeneration for the oracle is not timed)."""
+def dense_cpu_baselines(model, seconds):
+    """The oracle on all host threads (the headline baseline) and on one."""
+    allt = dense_cpu_baseline(model, seconds)
+    one = dense_cpu_baseline(model, max(2.0, seconds / 3), nth=1)
+    allt["one_thread"] = {k: one[k] for k in ("value", "unit", "tokens_per_s_equiv", "sample")}
+    allt["threads"] = allt["cores"]
+    allt["host"] = host_info()
+    return allt
+
+
+def dense_cpu_baseline(model, seconds, nth=None):
+    """The oracle (fp64) on the same pass: token after token, layer by layer
+    from token 0's carry, until `seconds` of oracle time have run (weight
+    regeneration for the oracle is not timed)."""
     import oracle
     t_oracle = 0.0
     nbytes = 0
-    nth = threads()
+    nth = threads() if nth is None else nth
     c = oracle.rms_carry(synth.x_vec(model.H, synth.seed_of(5, 999)).astype(np.float64), model.eps)
     layers_done = 0
     tok = 0
     while t_oracle < seconds:
         for l in range(model.L):
             fm = model.fmts
-            ws = [synth.blocks(fm[m], r, k, model.seed(l, m), threads=nth)
+            ws = [synth.blocks(fm[m], r, k, model.seed(l, m), threads=threads())
                   for m, (_, r, k) in enumerate(model.shapes)]
             t = time.perf_counter()
             y, _ = oracle.gemv_rows(fm[0], ws[0], *model.shapes[0][1:], c.astype(np.float32), threads=nth)
@@ -604,6 +745,8 @@ def q4_0_workload(args, dev):
     res = {
         "value": nbytes * 16 * n / (ms16 / 1e3) / 1e9,
         "ms_per_step": ms16 / n,
+        "pct_hbm_peak": 100.0 * nbytes * 16 * n / (ms16 / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "sha256_y": {"block_rows_0": sha256_of(y0), "block_rows_512": sha256_of(y512)},
         "config": {"workload": c["name"], "format": "Q4_0", "rows": rows, "k": k,
                    "launch": "one grid over 16 distinct matrices (151 MB), rotated over 128 copies"},
         "single_matrix": {"us_per_launch": ms1 / n * 1e3, "GBs": nbytes * n / (ms1 / 1e3) / 1e9,
@@ -666,10 +809,24 @@ def moe_workload(args, dev):
     wall, ms = _timed(token, n, torch)
     per_tok = 3 * ns * q.qgemv_weight_bytes(q.MXFP4, out, k)
     gbs = per_tok * n / wall / 1e9
+    # every token once more at each of the config's block sizes: the outputs
+    # must not depend on it (I1); their hashes are recorded (I4)
+    hashes, outs = {}, {}
+    for Bv in synth.CONFIGS[4]["block_rows"]:
+        B = Bv
+        for t in range(c["tokens"]):
+            token(t)
+        torch.cuda.synchronize()
+        outs[Bv] = y.clone()
+        hashes[f"block_rows_{Bv}"] = sha256_of(y)
+    B = args.block_rows
+    ref = outs[synth.CONFIGS[4]["block_rows"][0]]
+    same = all(bool(torch.equal(o.view(torch.int32), ref.view(torch.int32))) for o in outs.values())
     return {"value": gbs, "ms_per_step": wall / n * 1e3, "tokens_per_s": n / wall,
-            "bytes_per_token": per_tok,
+            "us_per_token": wall / n * 1e6, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+            "bytes_per_token": per_tok, "block_rows_bit_identical": same, "sha256_y_all_tokens": hashes,
             "config": {"workload": c["name"], "format": "MXFP4", "n_expert": E, "out": out, "k": k,
-                       "experts_per_token": ns, "tokens": n, "block_rows": B,
+                       "experts_per_token": ns, "tokens": n, "block_rows": args.block_rows,
                        "launches_per_token": "gate/up pair grid storing SiLU*up, down grid, combine",
                        "resident_bytes": 3 * q.qgemv_weight_bytes(q.MXFP4, rows, k)}}
 
@@ -756,7 +913,8 @@ def ffn_streamed_workload(args, dev):
             out[str(B)] = {"link_GBs": link, "ms_per_token": wall_s / n * 1e3,
                            "pct_of_256MiB_copy": 100 * link / link_256,
                            "copy_GBs_at_block_size": blk * 64 / (ms_c / 1e3) / 1e9,
-                           "bit_identical_to_resident": same, "ring_bytes": stv.ring_bytes}
+                           "bit_identical_to_resident": same, "ring_bytes": stv.ring_bytes,
+                           "sha256_y": sha256_of(y)}
     best = max(out, key=lambda b: out[b]["link_GBs"])
     # zero copy: the kernels read the pinned host weights in place over the link
     for _ in range(max(args.warmup, 1)):
@@ -769,8 +927,9 @@ def ffn_streamed_workload(args, dev):
               "bit_identical_to_resident": bool(torch.equal(y.view(torch.int32), ref.view(torch.int32)))}
     return {"value": out[best]["link_GBs"], "ms_per_step": out[best]["ms_per_token"], "unit_note":
             "host-link GB/s of the streamed pass (weight bytes copied / wall time)",
+            "pct_of_256MiB_copy": out[best]["pct_of_256MiB_copy"],
             "bytes_per_token": per_tok, "h2d_256MiB_GBs": link_256, "block_rows": out, "mapped": mapped,
-            "resident": resident,
+            "resident": resident, "sha256_y_resident": sha256_of(ref),
             "config": {"workload": c["name"], "format": "Q8_0", "hidden": H, "ffn": F,
                        "lookahead": c["lookahead"], "best_block_rows": int(best)}}
 
@@ -889,9 +1048,18 @@ def q8_0_small_workload(args, dev):
     n = max(args.steps, 200)
     wall, ms = _timed(one, n, torch)
     nbytes = w.numel()
-    return {"value": nbytes * n / (ms / 1e3) / 1e9, "ms_per_step": ms / n,
-            "config": {"workload": c["name"], "format": "Q8_0", "rows": rows, "k": k,
-                       "note": "weights stay in cache across launches; a latency figure, not an HBM one"}}
+    res = {"value": nbytes * n / (ms / 1e3) / 1e9, "ms_per_step": ms / n, "sha256_y": sha256_of(y),
+           "config": {"workload": c["name"], "format": "Q8_0", "rows": rows, "k": k,
+                      "note": "weights stay in cache across launches; a latency figure, not an HBM one"}}
+    if not args.no_check:
+        import oracle
+        ref, a = oracle.gemv_rows(oracle.Q8_0, w.cpu().numpy(), rows, k, x.cpu().numpy())
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        res["parity"] = {"max_componentwise": float(np.max(err / a)),
+                         "max_normwise": float(err.max() / np.abs(ref).max()), "tol": TOL,
+                         "pass": bool(np.all(err <= TOL * a) and err.max() <= TOL * np.abs(ref).max())}
+    return res
+
 
 def dense_batch_workload(args, dev):
     """The dense 20B-class pass (Q8_0, or --kquant for the Q4_K_M mix) with
@@ -980,6 +1148,48 @@ WORKLOADS = {"dense20b": dense_workload, "q4_0_4096": q4_0_workload, "moe_mxfp4"
              "moe_streamed": moe_streamed_workload}
 
 
+def extra_configs(args, dev):
+    """The other workloads, each reduced to the figures it is quoted with, for
+    the default run's line: Q8_0 256x1024 (latency, oracle parity), Q4_0
+    4096x4096 (16-matrix grid, block_rows 0 vs 512), the streamed Q8_0 FFN trio
+    (block_rows 128/512/2048 against the same run's pinned copy) and the MXFP4
+    MoE (64 tokens, block_rows 0/128/512)."""
+    import copy
+    import torch
+    out = {}
+    a = copy.copy(args)
+    a.warmup, a.steps = 2, 64
+    t = time.perf_counter()
+    r = q8_0_small_workload(a, dev)
+    out["q8_0_256x1024"] = {"us_per_launch": r["ms_per_step"] * 1e3, "GBs_cache_resident": r["value"],
+                            "parity": r.get("parity"), "note": r["config"]["note"]}
+    r = q4_0_workload(a, dev)
+    out["q4_0_4096x4096"] = {"GBs": r["value"], "pct_hbm_peak": r["pct_hbm_peak"],
+                             "us_per_grid": r["ms_per_step"] * 1e3, "launch": r["config"]["launch"],
+                             "single_matrix": r["single_matrix"],
+                             "block_rows_0_vs_512_bit_identical": r["block_rows_0_vs_512_bit_identical"],
+                             "sha256_y": r["sha256_y"], "parity": r.get("parity")}
+    torch.cuda.empty_cache()
+    a.steps = 8
+    r = ffn_streamed_workload(a, dev)
+    out["ffn_q8_0_streamed"] = {"link_GBs": r["value"], "pct_of_256MiB_copy": r["pct_of_256MiB_copy"],
+                                "best_block_rows": r["config"]["best_block_rows"],
+                                "h2d_256MiB_GBs": r["h2d_256MiB_GBs"], "lookahead": r["config"]["lookahead"],
+                                "block_rows": r["block_rows"], "mapped": r["mapped"], "resident": r["resident"],
+                                "sha256_y_resident": r["sha256_y_resident"]}
+    torch.cuda.empty_cache()
+    a.steps, a.block_rows = 0, 0
+    r = moe_workload(a, dev)
+    out["moe_mxfp4_top4"] = {"GBs": r["value"], "pct_hbm_peak": r["pct_hbm_peak"], "tokens_per_s": r["tokens_per_s"],
+                             "us_per_token": r["us_per_token"], "bytes_per_token": r["bytes_per_token"],
+                             "tokens": r["config"]["tokens"], "launches": r["config"]["launches_per_token"],
+                             "block_rows_bit_identical": r["block_rows_bit_identical"],
+                             "sha256_y_all_tokens": r["sha256_y_all_tokens"]}
+    torch.cuda.empty_cache()
+    out["extras_seconds"] = round(time.perf_counter() - t, 1)
+    return out
+
+
 # --- entry --------------------------------------------------------------------------
 
 def main(argv=None):
@@ -996,6 +1206,10 @@ def main(argv=None):
     p.add_argument("--separate", action="store_true", help="the default: 176 fused GEMV launches per token")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="dense20b only: skip the other workloads' figures and the read ceiling")
+    p.add_argument("--no-free-running", action="store_true",
+                   help="dense20b only: skip the oracle's own (free-running) pass of the first token")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--block-rows", type=int, default=0, help="block_rows for the MoE workload")
     p.add_argument("--batch", type=int, default=4, help="tokens per step of dense20b_batch")
@@ -1023,6 +1237,12 @@ def main(argv=None):
         del src, dst
     fn = WORKLOADS[args.workload]
     res = fn(args, dev)
+    if args.workload in ("dense20b", "q4_k_m_dense20b") and not args.no_extras:
+        ceil = read_ceiling(dev)
+        res["read_ceiling"] = ceil
+        res["pct_of_read_ceiling"] = 100.0 * res["value"] / ceil["GBs"]
+        if args.workload == "dense20b":
+            res.update(extra_configs(args, dev))
     line = {
         "metric": METRIC,
         "value": round(res.pop("value"), 3),

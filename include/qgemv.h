@@ -292,6 +292,17 @@ int qgemv_combine(const float *y, int64_t y_stride, int32_t n_sel, const float *
 int qgemv_rms_carry(const float *v, float *out, int64_t n, float eps, int32_t gelu,
                     qg_stream_t stream);
 
+/* A measurement aid: one plain streaming read of n_bytes of device memory at
+ * data (a positive multiple of 16 bytes, 16-byte aligned), 2048 workgroups of
+ * 256 lanes each reading one 16-byte granule per step with the weights'
+ * non-temporal hint; an xor of everything read is xor-ed into *sink (device
+ * uint32), so the loads cannot be dropped.  Its rate is the read ceiling the
+ * GEMV's weight stream is compared with: the bandwidth term of neurostream
+ * README, "The idea" (tokens/sec = effective bandwidth / active bytes per
+ * token), measured rather than taken from the specification.  QG_E_NULL,
+ * QG_E_ARG (size or alignment); asynchronous on `stream`. */
+int qgemv_read_ceiling(const void *data, int64_t n_bytes, uint32_t *sink, qg_stream_t stream);
+
 /* Decoded fp32 weights of rows [row_start, row_end): out is device memory of
  * (row_end - row_start) * k floats, row-major.  Uses the GEMV kernels' own
  * block decoders; a test aid for the bit-exact decode check. */

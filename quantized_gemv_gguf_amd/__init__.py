@@ -98,6 +98,7 @@ def lib():
         "qgemv_silu_mul": ([_vp, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_rms_carry": ([_vp, _vp, _i64, ctypes.c_float, _i32, _vp], ctypes.c_int),
         "qgemv_dequant_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp], ctypes.c_int),
+        "qgemv_read_ceiling": ([_vp, _i64, _vp, _vp], ctypes.c_int),
         "qgemv_stream_create": ([_i64, _i32, P(_vp)], ctypes.c_int),
         "qgemv_stream_ring_bytes": ([_vp], _i64),
         "qgemv_stream_rows": ([_vp, P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
@@ -360,6 +361,16 @@ def qgemv_rms_carry(v, out, eps: float = 1e-6, gelu: bool = False, stream=None) 
     n = v.numel()
     _check(lib().qgemv_rms_carry(_f32(v, n, "v"), _f32(out, n, "out"), n, float(eps), int(bool(gelu)),
                                  _stream(stream)), "qgemv_rms_carry")
+
+
+def qgemv_read_ceiling(data, sink, stream=None) -> None:
+    """One plain streaming read of the device tensor ``data`` (its whole
+    storage; a multiple of 16 bytes); the xor of what was read is xor-ed into
+    the uint32/int32 device tensor ``sink``."""
+    n = data.numel() * data.element_size()
+    if not data.is_cuda or not sink.is_cuda or sink.element_size() != 4:
+        raise ValueError("data and sink must be device tensors, sink 32-bit")
+    _check(lib().qgemv_read_ceiling(_ptr(data), n, _ptr(sink), _stream(stream)), "qgemv_read_ceiling")
 
 
 def qgemv_dequant_rows(w: Matrix, row_start: int, row_end: int, out, stream=None) -> None:

@@ -127,6 +127,24 @@ __global__ void combine_kernel(const float *y, int64_t y_stride, int n_sel, cons
   }
 }
 
+// Plain streaming read of n16 16-byte granules: every lane reads one granule
+// per iteration, grid-stride, with the weights' non-temporal hint, and folds
+// it into an xor so the loads are live; each wave adds one atomic xor to
+// *sink.  The bandwidth a kernel that only reads reaches on this device: the
+// ceiling the GEMV's weight stream is compared with.
+constexpr int kReadGroups = 2048, kReadThreads = 256;
+__global__ void __launch_bounds__(kReadThreads) read_kernel(const u32x4 *p, int64_t n16, uint32_t *sink) {
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+}
+
 constexpr int kCarryThreads = 1024;
 constexpr int kMaxRmsK = 32 * kCarryThreads;  // largest k whose fused RMS matches qgemv_rms_carry's order
 
@@ -1250,6 +1268,15 @@ int qgemv_combine(const float *y, int64_t y_stride, int32_t n_sel, const float *
   if (!out || (n_sel > 0 && (!y || !w))) return QG_E_NULL;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, y_stride, n_sel, w, n, out);
+  QG_HIP(hipGetLastError());
+  return QG_OK;
+}
+
+int qgemv_read_ceiling(const void *data, int64_t n_bytes, uint32_t *sink, qg_stream_t stream) {
+  if (!data || !sink) return QG_E_NULL;
+  if (n_bytes <= 0 || n_bytes % 16 != 0 || ((uintptr_t)data & 15)) return QG_E_ARG;
+  hipLaunchKernelGGL(read_kernel, dim3(kReadGroups), dim3(kReadThreads), 0, stream, (const u32x4 *)data,
+                     n_bytes / 16, sink);
   QG_HIP(hipGetLastError());
   return QG_OK;
 }

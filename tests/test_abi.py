@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 31, names
+    assert len(names) == 32, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -186,6 +186,16 @@ def test_elementwise_validation():
     assert L.qgemv_rms_carry(FAKE, FAKE, 4, float("nan"), 0, None) == E_ARG
     assert L.qgemv_rms_carry(FAKE, FAKE, 4, 1e-6, 2, None) == E_ARG
     assert L.qgemv_rms_carry(0, FAKE, 4, 1e-6, 0, None) == E_NULL
+
+
+def test_read_ceiling_validation():
+    L = q.lib()
+    sink = ctypes.c_void_p(0x1000)
+    assert L.qgemv_read_ceiling(None, 16, sink, None) == E_NULL
+    assert L.qgemv_read_ceiling(FAKE, 16, None, None) == E_NULL
+    assert L.qgemv_read_ceiling(FAKE, 0, sink, None) == E_ARG
+    assert L.qgemv_read_ceiling(FAKE, 24, sink, None) == E_ARG       # not a multiple of 16
+    assert L.qgemv_read_ceiling(FAKE + 8, 32, sink, None) == E_ARG   # not 16-byte aligned
 
 
 def test_streamer_validation():
