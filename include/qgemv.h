@@ -343,6 +343,23 @@ int qgemv_stream_rows(qg_streamer *st, const qg_matrix *w, int64_t row_start,
 int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win,
                          int32_t n_win, int64_t block_rows, qg_stream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qgemv_stream_rows with no
+ * streamer and no allocation of any kind.  The ring is a device array of
+ * QG_NOALLOC_RING_BYTES inside the library (one per GPU, held until the
+ * process ends), used as two slots of half that size: block j of the window
+ * is copied into slot j mod 2 with hipMemcpyAsync on `stream` and multiplied
+ * there by the same kernel as qgemv_rows, so y has qgemv_rows's bits.  Copies
+ * and kernels share `stream`: they run one after the other, with no
+ * copy/compute overlap.  A block of more than QG_NOALLOC_RING_BYTES / 2
+ * bytes gives QG_E_CAPACITY, pageable or device weights QG_E_NOT_PINNED.
+ * Every call on a GPU uses that GPU's one ring: calls that overlap on one GPU
+ * (on different streams, or from several threads) race and must not be
+ * made. */
+#define QG_NOALLOC_RING_BYTES (32ll << 20)
+int qgemv_stream_rows_noalloc(const qg_matrix *w, int64_t row_start, int64_t row_end,
+                              int64_t block_rows, const float *x, float *y, qg_stream_t stream);
+
 /* Waits for the streamer's work, frees it.  NULL is a no-op. */
 int qgemv_stream_destroy(qg_streamer *st);
 

@@ -104,6 +104,7 @@ def lib():
         "qgemv_stream_rows": ([_vp, P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
         "qgemv_stream_windows": ([_vp, _i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_stream_destroy": ([_vp], ctypes.c_int),
+        "qgemv_stream_rows_noalloc": ([P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
         "qgemv_mapped_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_mapped_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_chain_create": ([_i32, P(qg_chain_step), _i32, P(qg_chain_window), _i32, P(_vp)], ctypes.c_int),
@@ -423,6 +424,19 @@ class Streamer:
             self.close()
         except Exception:
             pass
+
+
+NOALLOC_RING_BYTES = 32 << 20
+
+
+def qgemv_stream_rows_noalloc(w: Matrix, row_start: int, row_end: int, x, y, block_rows: int = 0,
+                              stream=None) -> None:
+    """Streamed rows through the library's own two-slot ring (no allocation;
+    blocks up to NOALLOC_RING_BYTES / 2 bytes; calls must not overlap on a GPU)."""
+    m = w.c()
+    n = max(row_end - row_start, 0)
+    _check(lib().qgemv_stream_rows_noalloc(ctypes.byref(m), row_start, row_end, block_rows, _f32(x, w.k, "x"),
+                                           _f32(y, n, "y"), _stream(stream)), "qgemv_stream_rows_noalloc")
 
 
 def qgemv_stream_create(slot_bytes: int, lookahead: int) -> Streamer:

@@ -1490,6 +1490,68 @@ int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_windo
   return stream_windows(st, fmt, k, win, n_win, block_rows, stream);
 }
 
+// ---- streaming without allocation -----------------------------------------------
+//
+// The ring of qgemv_stream_rows_noalloc: a file-scope device array, one per
+// GPU the library runs on, held until the process ends.  In host code its
+// name is only a stand-in; the device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[QG_NOALLOC_RING_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+// The current device's copy of `scratch`.
+int scratch_of_device(uint8_t **out) {
+  int dev = 0;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return QG_E_ARG;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    QG_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (uint8_t *)g_scratch_ptr[dev];
+  return QG_OK;
+}
+
+}  // namespace
+
+int qgemv_stream_rows_noalloc(const qg_matrix *w, int64_t row_start, int64_t row_end, int64_t block_rows,
+                              const float *x, float *y, qg_stream_t stream) {
+  int rc = check_matrix(w);
+  if (rc) return rc;
+  if ((rc = check_range(w->n_rows, row_start, row_end))) return rc;
+  if (block_rows < 0) return QG_E_ARG;
+  if (row_end == row_start) return QG_OK;
+  if (!x || !y) return QG_E_NULL;
+  const int64_t rb = row_bytes_of(w->fmt, w->k);
+  const int64_t len = row_end - row_start;
+  const int64_t B = block_rows > 0 ? std::min(block_rows, len) : len;
+  constexpr int64_t kSlot = QG_NOALLOC_RING_BYTES / 2;
+  if (B * rb > kSlot) return QG_E_CAPACITY;
+  if ((rc = check_pinned(w->data))) return rc;
+  uint8_t *ring = nullptr;
+  if ((rc = scratch_of_device(&ring))) return rc;
+  // Block j goes to slot j mod 2; its copy and its kernel are both on
+  // `stream`, so the copy into a slot always follows the kernel that last
+  // read it.
+  int j = 0;
+  for (int64_t r = row_start; r < row_end; r += B, ++j) {
+    const int64_t n = std::min(B, row_end - r);
+    uint8_t *dst = ring + (j & 1) * kSlot;
+    QG_HIP(hipMemcpyAsync(dst, (const uint8_t *)w->data + r * rb, (size_t)(n * rb), hipMemcpyHostToDevice,
+                          (hipStream_t)stream));
+    qg_window blk = {dst, n, 0, n, x, y + (r - row_start)};
+    if ((rc = launch_gemv(w->fmt, w->k, &blk, 1, 0, (hipStream_t)stream))) return rc;
+  }
+  return QG_OK;
+}
+
 // ---- host-mapped weights: the kernels read page-locked host memory in place ----
 
 int qgemv_mapped_rows(const qg_matrix *w, int64_t row_start, int64_t row_end, const float *x, float *y,

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 32, names
+    assert len(names) == 33, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -196,6 +196,18 @@ def test_read_ceiling_validation():
     assert L.qgemv_read_ceiling(FAKE, 0, sink, None) == E_ARG
     assert L.qgemv_read_ceiling(FAKE, 24, sink, None) == E_ARG       # not a multiple of 16
     assert L.qgemv_read_ceiling(FAKE + 8, 32, sink, None) == E_ARG   # not 16-byte aligned
+
+
+def test_stream_rows_noalloc_validation():
+    L = q.lib()
+    assert L.qgemv_stream_rows_noalloc(None, 0, 1, 0, FAKE, FAKE, None) == E_NULL
+    assert L.qgemv_stream_rows_noalloc(ctypes.byref(mat()), 0, 9, 0, FAKE, FAKE, None) == E_RANGE
+    assert L.qgemv_stream_rows_noalloc(ctypes.byref(mat()), 0, 1, -1, FAKE, FAKE, None) == E_ARG
+    assert L.qgemv_stream_rows_noalloc(ctypes.byref(mat()), 0, 1, 0, 0, FAKE, None) == E_NULL
+    assert L.qgemv_stream_rows_noalloc(ctypes.byref(mat(fmt=0)), 0, 1, 0, FAKE, FAKE, None) == E_FMT
+    assert L.qgemv_stream_rows_noalloc(ctypes.byref(mat()), 1, 1, 0, 0, 0, None) == 0  # empty window
+    text = open(HEADER).read()
+    assert f"#define QG_NOALLOC_RING_BYTES ({q.NOALLOC_RING_BYTES >> 20}ll << 20)" in text
 
 
 def test_streamer_validation():
