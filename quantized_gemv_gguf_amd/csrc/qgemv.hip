@@ -618,6 +618,7 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
     }
     const bool rms = S.in_op == QG_IN_RMS || S.in_op == QG_IN_GELU_RMS;
     int xw = -1;
+    const float *cxp = nullptr, *cx2p = nullptr;  // inputs of the registered x
     if (rms) {
       // Every window of an RMS step shares x: normalise it once for the step.
       // Column c of a lane's blocks is its own 64-block run, summed like one
@@ -702,8 +703,15 @@ chain_kernel(const ChainStepDev *steps_g, int n_steps, const ChainWinDev *wins_g
       const bool now = more && (wid != 0 || nx.s == s);
       deferred = more && !now;
       if (xw != INT32_MAX && cur.w != xw) {
+        // (a window with the inputs already in registers keeps them: a reload
+        // would also wait for the weight prefetch, the load counter being in
+        // order)
         const ChainWinDev W = S.n_win > 1 ? load_win(wins + S.win0 + cur.w) : S.w0;
-        load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
+        if (xw < 0 || W.x != cxp || (S.in_op == QG_IN_SILU_MUL && W.x2 != cx2p)) {
+          load_x(W.x, W.x2, S.in_op == QG_IN_SILU_MUL, S.nb, ro.wit);
+          cxp = W.x;
+          cx2p = W.x2;
+        }
         xw = cur.w;
       }
       const int nrows = cur.nrows;

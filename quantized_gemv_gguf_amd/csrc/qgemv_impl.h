@@ -800,13 +800,17 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     issue(fp, s);
     advance_fetch();
   }
-  int xw = CW.w;
+  // The activations in registers are those of (x, x2): a tile of another
+  // window with the same inputs keeps them (reloading would also wait for
+  // every weight copy in flight, since the load counter drains in order).
+  const float *cx = CW.x, *cx2 = CW.x2;
   int slot = 0;  // ring slot of the row being computed
   int parity = 0;
   for (;;) {
-    if (CW.w != xw) {
+    if (CW.x != cx || (in_op == QG_IN_SILU_MUL && CW.x2 != cx2)) {
       load_x(CW.x, CW.x2);
-      xw = CW.w;
+      cx = CW.x;
+      cx2 = CW.x2;
     }
     const int nrows = cur.nrows;
     // Alignment phase of the tile's rows: row i of the tile sits at
