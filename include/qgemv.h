@@ -135,8 +135,9 @@ typedef struct qg_window {
 /* Bytes per block: 34, 18, 17, 144 or 210; QG_E_FMT for an unknown format. */
 int64_t qgemv_block_bytes(int32_t fmt);
 
-/* Weights per block (QK): 32, or 256 for Q4_K and Q6_K; QG_E_FMT for an
- * unknown format. */
+/* Weights per block (QK): 32, or 256 for Q4_K and Q6_K (RAMforge README,
+ * "Milestone 5": 32-weight Q8_0/Q4_0 blocks, the 256-weight Q4_K
+ * super-block); QG_E_FMT for an unknown format. */
 int64_t qgemv_block_weights(int32_t fmt);
 
 /* Bytes of an n_rows x k matrix, or a negative status (QG_E_FMT, QG_E_SHAPE). */
@@ -212,8 +213,11 @@ int qgemv_rows_op(const qg_matrix *w, int64_t row_start, int64_t row_end, const 
                   int64_t block_rows, qg_stream_t stream);
 
 /* Several row windows (any matrices of the same fmt and k, each with its own
- * x and y) computed by ONE grid.  win is a host array of n_win entries,
- * 0 <= n_win <= QG_MAX_WINDOWS; n_win = 0 is a no-op. */
+ * x and y) computed by ONE grid: the row-bounded walks of neurostream README,
+ * "How it works" (stream_linear over [row_start, row_end), for example the
+ * selected experts' rows), launched together instead of one after another.
+ * win is a host array of n_win entries, 0 <= n_win <= QG_MAX_WINDOWS;
+ * n_win = 0 is a no-op. */
 int qgemv_windows(int32_t fmt, int64_t k, const qg_window *win, int32_t n_win,
                   int64_t block_rows, qg_stream_t stream);
 
@@ -304,8 +308,12 @@ int qgemv_rms_carry(const float *v, float *out, int64_t n, float eps, int32_t ge
 int qgemv_read_ceiling(const void *data, int64_t n_bytes, uint32_t *sink, qg_stream_t stream);
 
 /* Decoded fp32 weights of rows [row_start, row_end): out is device memory of
- * (row_end - row_start) * k floats, row-major.  Uses the GEMV kernels' own
- * block decoders; a test aid for the bit-exact decode check. */
+ * (row_end - row_start) * k floats, row-major; each weight is the format's
+ * value (RAMforge README, "Milestone 5") rounded once to fp32, which for
+ * every generated block is exact.  A test aid for the bit-exact decode check
+ * (neurostream README, "Supported": bit-exact decode against the reference
+ * gguf implementation): Q4_0 and the K-quants build the weights from the same
+ * code formation as the GEMV's dot, Q8_0 and MXFP4 from the same decoder. */
 int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
                        float *out, qg_stream_t stream);
 
@@ -435,14 +443,23 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
  * device, which must be current), of one workgroup per compute unit: all of
  * them must be resident together, so nothing else may occupy compute units
  * while it runs.  Runs of one chain must not overlap: they share its barrier
- * state.  A barrier that waits longer than a few seconds gives up, and
- * qgemv_chain_check reports it. */
+ * state.  A barrier that waits longer than its spin limit (a few seconds by
+ * default) gives up, marks the chain failed and lets the run finish with
+ * undefined outputs.  Once a failure is visible to the host (a page-locked
+ * word the failing barrier writes; no waiting is involved), qgemv_chain_run
+ * enqueues nothing and returns QG_E_BARRIER until qgemv_chain_check has
+ * reset the state (a failure of a run still in flight is seen by the next
+ * call to qgemv_chain_check). */
 int qgemv_chain_run(qg_chain *c, qg_stream_t stream);
 
 /* Waits for the device, then QG_OK, or QG_E_BARRIER if a run's barrier gave
- * up (workgroups not all resident; its outputs are then undefined, and the
- * state is reset for the next run). */
+ * up since the last check (workgroups not all resident; those outputs are
+ * undefined), after resetting the state for the next run. */
 int qgemv_chain_check(qg_chain *c);
+
+/* Polls (>= 1) a barrier waits before it gives up; the default is 2^22.
+ * Waits for the device.  QG_E_ARG for 0 or on another device. */
+int qgemv_chain_set_spin_limit(qg_chain *c, uint32_t polls);
 
 /* Workgroups a run launches (one per compute unit), or a negative status. */
 int64_t qgemv_chain_grid(const qg_chain *c);

@@ -110,6 +110,7 @@ def lib():
         "qgemv_chain_create": ([_i32, P(qg_chain_step), _i32, P(qg_chain_window), _i32, P(_vp)], ctypes.c_int),
         "qgemv_chain_run": ([_vp, _vp], ctypes.c_int),
         "qgemv_chain_check": ([_vp], ctypes.c_int),
+        "qgemv_chain_set_spin_limit": ([_vp, ctypes.c_uint32], ctypes.c_int),
         "qgemv_chain_grid": ([_vp], _i64),
         "qgemv_chain_destroy": ([_vp], ctypes.c_int),
         "qgemv_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -506,6 +507,10 @@ class Chain:
 
     def check(self) -> None:
         _check(lib().qgemv_chain_check(self._h), "qgemv_chain_check")
+
+    def set_spin_limit(self, polls: int) -> None:
+        """Polls (>= 1) a barrier waits before it gives up (default 2^22)."""
+        _check(lib().qgemv_chain_set_spin_limit(self._h, int(polls)), "qgemv_chain_set_spin_limit")
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -240,7 +240,7 @@ constexpr int kChainWaves = 12;
 // Rows per chain tile: the tile cap of gemv_kernel, one row less at two
 // columns per lane (the chain keeps more state in registers).
 template <int FMT, int C> struct ChainRows { static constexpr int value = TileCap<FMT, C>::value - (C == 2 ? 1 : 0); };
-constexpr unsigned kSpinLimit = 1u << 22;  // barrier polls before giving up (seconds)
+constexpr unsigned kSpinLimit = 1u << 22;  // default barrier polls before giving up (seconds)
 
 struct ChainWinDev {
   const uint8_t *base;
@@ -274,6 +274,11 @@ constexpr int kMaxChainGroups = 1024;
 struct ChainSync {
   unsigned count, pad0[63];
   unsigned fail, pad1[63];
+  // Set by the host: a page-locked host word that a failing barrier also
+  // marks (the host reads it without waiting for the device), and the polls
+  // a barrier waits before it gives up.
+  unsigned *host_fail;
+  unsigned spin_limit, pad2[61];
   struct { unsigned gen, pad[63]; } flag[kMaxChainGroups];  // one line per workgroup
 };
 
@@ -291,8 +296,9 @@ constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt u
 //     to every workgroup's line.
 //   wait: unless last, poll the own line until it reaches `target`, then
 //     acquire.
-// A barrier still incomplete after kSpinLimit polls marks `fail` and lets the
-// workgroup through, so the kernel always ends; the host reports it.
+// A barrier still incomplete after spin_limit polls marks `fail` (and the
+// host's word) and lets the workgroup through, so the kernel always ends; the
+// host reports it.
 __device__ __forceinline__ bool chain_arrive(ChainSync *sy, unsigned n_groups, unsigned target, int wid) {
   __syncthreads();
   bool last = false;
@@ -316,17 +322,19 @@ __device__ __forceinline__ bool chain_arrive(ChainSync *sy, unsigned n_groups, u
 
 __device__ __forceinline__ void chain_wait(ChainSync *sy, unsigned target, bool last, int wid) {
   if (wid == 0 && !last) {
+    const unsigned limit = sy->spin_limit;
     for (unsigned spins = 1;; ++spins) {
       const unsigned g = __builtin_amdgcn_readfirstlane(
           __hip_atomic_load(&sy->flag[blockIdx.x].gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       if ((int)(g - target) >= 0) break;
-      if ((spins & 63) == 0) {
-        const unsigned f = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(&sy->fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (f || spins >= kSpinLimit) {
-          __hip_atomic_store(&sy->fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+      bool give_up = spins >= limit;
+      if ((spins & 63) == 0)
+        give_up |= __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(&sy->fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
+      if (give_up) {
+        __hip_atomic_store(&sy->fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sy->host_fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
@@ -1601,6 +1609,8 @@ struct qg_chain {
   int grid;
   unsigned gen;  // barrier generation at the start of the next run
   void *mem;  // one device allocation: steps, windows, tile prefixes, barrier state
+  unsigned *host_fail;  // page-locked, mapped: a failed barrier's mark, read without waiting
+  unsigned spin_limit;
   ChainStepDev *steps;
   ChainWinDev *wins;
   int32_t *prefix;
@@ -1622,6 +1632,15 @@ ChainFn chain_fn(int32_t fmt) {
 }
 
 bool rms_op(int32_t op) { return op == QG_IN_RMS || op == QG_IN_GELU_RMS; }
+
+// Writes the host-set fields of a chain's barrier state (after it was zeroed).
+hipError_t sync_host_fields(ChainSync *sy, unsigned *host_fail, unsigned spin_limit) {
+  void *dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&dev, host_fail, 0);
+  if (e != hipSuccess) return e;
+  if ((e = hipMemcpy(&sy->host_fail, &dev, sizeof(dev), hipMemcpyHostToDevice)) != hipSuccess) return e;
+  return hipMemcpy(&sy->spin_limit, &spin_limit, sizeof(spin_limit), hipMemcpyHostToDevice);
+}
 
 int validate_chain(int32_t fmt, const qg_chain_step *steps, int32_t n_steps, const qg_chain_window *win,
                    int32_t n_win) {
@@ -1773,8 +1792,20 @@ int qgemv_chain_create(int32_t fmt, const qg_chain_step *steps, int32_t n_steps,
   if ((e = hipMemcpy(mem + o_pre, hp.data(), sizeof(int32_t) * hp.size(), hipMemcpyHostToDevice)))
     return fail(e, "hipMemcpy(prefix)");
   if ((e = hipMemset(mem + o_sync, 0, sizeof(ChainSync)))) return fail(e, "hipMemset(sync)");
-  if ((e = hipDeviceSynchronize())) return fail(e, "hipDeviceSynchronize");
+  unsigned *hf = nullptr;
+  if ((e = hipHostMalloc((void **)&hf, sizeof(unsigned), hipHostMallocMapped))) return fail(e, "hipHostMalloc(fail)");
+  *hf = 0;
+  if ((e = sync_host_fields((ChainSync *)(mem + o_sync), hf, kSpinLimit))) {
+    (void)hipHostFree(hf);
+    return fail(e, "hipMemcpy(sync fields)");
+  }
+  if ((e = hipDeviceSynchronize())) {
+    (void)hipHostFree(hf);
+    return fail(e, "hipDeviceSynchronize");
+  }
   qg_chain *c = new qg_chain;
+  c->host_fail = hf;
+  c->spin_limit = kSpinLimit;
   c->device = dev;
   c->fmt = fmt;
   c->n_steps = n_steps;
@@ -1794,6 +1825,9 @@ int qgemv_chain_run(qg_chain *c, qg_stream_t stream) {
   int dev = 0;
   QG_HIP(hipGetDevice(&dev));
   if (dev != c->device) return QG_E_ARG;
+  // An earlier run's barrier gave up (as far as the host can see without
+  // waiting): the barrier state is stale until qgemv_chain_check resets it.
+  if (__atomic_load_n(c->host_fail, __ATOMIC_ACQUIRE)) return QG_E_BARRIER;
   // An ordinary launch of exactly as many workgroups as the device holds at
   // once, so on a device running nothing else every workgroup is resident.
   // (Should one not be, the barrier gives up after a bounded wait instead of
@@ -1813,11 +1847,25 @@ int qgemv_chain_check(qg_chain *c) {
   QG_HIP(hipDeviceSynchronize());
   unsigned fail = 0;
   QG_HIP(hipMemcpy(&fail, &c->sync->fail, sizeof(fail), hipMemcpyDeviceToHost));
-  if (!fail) return QG_OK;
+  if (!fail && !__atomic_load_n(c->host_fail, __ATOMIC_ACQUIRE)) return QG_OK;
   QG_HIP(hipMemset(c->sync, 0, sizeof(ChainSync)));
+  QG_HIP(sync_host_fields(c->sync, c->host_fail, c->spin_limit));
   QG_HIP(hipDeviceSynchronize());
+  __atomic_store_n(c->host_fail, 0u, __ATOMIC_RELEASE);
   c->gen = 0;
   return QG_E_BARRIER;
+}
+
+int qgemv_chain_set_spin_limit(qg_chain *c, uint32_t polls) {
+  if (!c) return QG_E_NULL;
+  if (polls < 1) return QG_E_ARG;
+  int dev = 0;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != c->device) return QG_E_ARG;
+  QG_HIP(hipDeviceSynchronize());
+  QG_HIP(hipMemcpy(&c->sync->spin_limit, &polls, sizeof(polls), hipMemcpyHostToDevice));
+  c->spin_limit = polls;
+  return QG_OK;
 }
 
 int64_t qgemv_chain_grid(const qg_chain *c) { return c ? (int64_t)c->grid : (int64_t)QG_E_NULL; }
@@ -1826,7 +1874,9 @@ int qgemv_chain_destroy(qg_chain *c) {
   if (!c) return QG_OK;
   hipError_t e = hipDeviceSynchronize();
   hipError_t f = hipFree(c->mem);
+  hipError_t h = hipHostFree(c->host_fail);
   delete c;
+  if (f == hipSuccess) f = h;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   if (f != hipSuccess) return hip_fail(f, "hipFree");
   return QG_OK;

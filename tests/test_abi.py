@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -438,6 +438,7 @@ def test_chain_validation():
     assert create([cstep(op=1, n=2)], [cwin(), cwin(x=FAKE + 256)]) == E_ARG
     assert L.qgemv_chain_run(None, None) == E_NULL
     assert L.qgemv_chain_check(None) == E_NULL
+    assert L.qgemv_chain_set_spin_limit(None, 1 << 20) == E_NULL
     assert L.qgemv_chain_grid(None) == E_NULL
     assert L.qgemv_chain_destroy(None) == 0
 

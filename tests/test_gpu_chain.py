@@ -276,3 +276,35 @@ def test_chain_many_steps_and_silu(dev):
     torch.cuda.synchronize()
     for s in range(120):
         assert bits_equal(host(ys[s]), host(ref[s])), f"step {s}"
+
+
+def test_chain_barrier_failure_is_reported_and_reset(dev):
+    """A barrier that gives up (forced from the host: a spin limit of one poll,
+    far below the time a device-wide barrier takes) lets the run finish with
+    undefined outputs; once the host can see the failure, run enqueues nothing
+    and reports QG_E_BARRIER until check resets the state; after that, runs
+    are correct again."""
+    import torch
+    dense = Dense(dev, q.Q8_0, 1024, 2048, 2, seed=8100)
+    with q.Chain(q.Q8_0, dense.steps()) as c:
+        c.run()
+        c.check()
+        torch.cuda.synchronize()
+        good = [y.cpu().numpy().copy() for y in dense.y]
+        c.set_spin_limit(1)
+        c.run()
+        torch.cuda.synchronize()
+        with pytest.raises(q.QgemvError) as e:
+            c.run()
+        assert e.value.status == -9
+        with pytest.raises(q.QgemvError) as e:
+            c.check()
+        assert e.value.status == -9
+        c.set_spin_limit(1 << 22)
+        for y in dense.y:
+            y.fill_(float("nan"))
+        c.run()
+        c.check()
+        torch.cuda.synchronize()
+        for s, y in enumerate(dense.y):
+            assert bits_equal(y.cpu().numpy(), good[s]), f"step {s}"
