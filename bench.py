@@ -915,7 +915,28 @@ def ffn_streamed_workload(args, dev):
                            "copy_GBs_at_block_size": blk * 64 / (ms_c / 1e3) / 1e9,
                            "bit_identical_to_resident": same, "ring_bytes": stv.ring_bytes,
                            "sha256_y": sha256_of(y)}
-    best = max(out, key=lambda b: out[b]["link_GBs"])
+    # the same walk as a streamed plan (one graph per token: no per-block host work)
+    P = [q.Matrix(pin[0], q.Q8_0, F, H), q.Matrix(pin[1], q.Q8_0, F, H), q.Matrix(pin[2], q.Q8_0, H, F)]
+    plans = {}
+    for B in (128, 512, 2048):
+        steps = [q.PlanGemv([q.Window(P[0], 0, F, x, g), q.Window(P[1], 0, F, x, u)], B),
+                 q.PlanSiluMul(g, u, hh), q.PlanGemv([q.Window(P[2], 0, H, hh, y)], B)]
+        with q.StreamPlan(B * rb_down, c["lookahead"], steps) as plan:
+            for _ in range(max(args.warmup, 1)):
+                plan.run()
+            torch.cuda.synchronize()
+            n = max(args.steps, 8)
+            wall_p, _ = _timed(lambda i: plan.run(), n, torch)
+            same = bool(torch.equal(y.view(torch.int32), ref.view(torch.int32)))
+            link = per_tok * n / wall_p / 1e9
+            plans[str(B)] = {"link_GBs": link, "ms_per_token": wall_p / n * 1e3,
+                             "pct_of_256MiB_copy": 100 * link / link_256, "bit_identical_to_resident": same,
+                             "ring_bytes": plan.ring_bytes}
+    for B, r in plans.items():
+        out[B]["plan"] = r
+    best = max(out, key=lambda b: max(out[b]["link_GBs"], out[b]["plan"]["link_GBs"]))
+    best_kind = "plan" if out[best]["plan"]["link_GBs"] > out[best]["link_GBs"] else "ring"
+    best_rate = max(out[best]["link_GBs"], out[best]["plan"]["link_GBs"])
     # zero copy: the kernels read the pinned host weights in place over the link
     for _ in range(max(args.warmup, 1)):
         run(pin, mapped=True)
@@ -925,9 +946,9 @@ def ffn_streamed_workload(args, dev):
     link_m = per_tok * n / wall_m / 1e9
     mapped = {"link_GBs": link_m, "ms_per_token": wall_m / n * 1e3, "pct_of_256MiB_copy": 100 * link_m / link_256,
               "bit_identical_to_resident": bool(torch.equal(y.view(torch.int32), ref.view(torch.int32)))}
-    return {"value": out[best]["link_GBs"], "ms_per_step": out[best]["ms_per_token"], "unit_note":
+    return {"value": best_rate, "ms_per_step": per_tok / best_rate / 1e6, "unit_note":
             "host-link GB/s of the streamed pass (weight bytes copied / wall time)",
-            "pct_of_256MiB_copy": out[best]["pct_of_256MiB_copy"],
+            "pct_of_256MiB_copy": 100 * best_rate / link_256, "best_mode": best_kind,
             "bytes_per_token": per_tok, "h2d_256MiB_GBs": link_256, "block_rows": out, "mapped": mapped,
             "resident": resident, "sha256_y_resident": sha256_of(ref),
             "config": {"workload": c["name"], "format": "Q8_0", "hidden": H, "ffn": F,
@@ -1019,6 +1040,33 @@ def moe_streamed_workload(args, dev):
                 measure(f"ring_B{B}_lookahead{la}", streamer=st, B=B)
                 legs[f"ring_B{B}_lookahead{la}"]["ring_bytes"] = st.ring_bytes
     measure("mapped", mapped=True)
+    # streamed plans: one graph per token, re-pointed at the token's experts
+    x = torch.empty(k, **f32)
+    sel0 = [int(e) for e in ids[0]]
+    Pm = [q.Matrix(w, q.MXFP4, rows, k) for w in pin]
+    gw = [q.Window(Pm[m], e * out, (e + 1) * out, x, gu[(m * ns + s) * out:(m * ns + s + 1) * out])
+          for m in range(2) for s, e in enumerate(sel0)]
+    dw = [q.Window(Pm[2], e * out, (e + 1) * out, h[s * out:(s + 1) * out], ye[s * out:(s + 1) * out])
+          for s, e in enumerate(sel0)]
+    for B, la in ((128, 1), (512, 1), (512, 2), (out, 2)):
+        steps = [q.PlanGemv(gw, B), q.PlanSiluMul(gu[:ns * out], gu[ns * out:], h), q.PlanGemv(dw, B)]
+        with q.StreamPlan(B * rb, la, steps) as plan:
+            def ptoken(t):
+                t = t % c["tokens"]
+                for s_, e in enumerate(ids[t]):
+                    for m in range(3):
+                        plan.set_rows(m * ns + s_, int(e) * out)
+                x.copy_(xs[t])
+                plan.run()
+            for t in range(max(args.warmup, 1)):
+                ptoken(t)
+            torch.cuda.synchronize()
+            wall, _ = _timed(ptoken, n, torch)
+            same = bool(torch.equal(ye.view(torch.int32), refs[(n - 1) % len(refs)].view(torch.int32)))
+            link = per_tok * n / wall / 1e9
+            legs[f"plan_B{B}_lookahead{la}"] = {"link_GBs": link, "us_per_token": wall / n * 1e6,
+                                                "pct_of_256MiB_copy": 100 * link / link_256,
+                                                "bit_identical_to_resident": same, "ring_bytes": plan.ring_bytes}
     best = max(legs, key=lambda kk: legs[kk]["link_GBs"])
     return {"value": legs[best]["link_GBs"], "ms_per_step": legs[best]["us_per_token"] / 1e3,
             "unit_note": "host-link GB/s of the selected experts' bytes per token (bytes / wall time)",
@@ -1173,7 +1221,7 @@ def extra_configs(args, dev):
     a.steps = 8
     r = ffn_streamed_workload(a, dev)
     out["ffn_q8_0_streamed"] = {"link_GBs": r["value"], "pct_of_256MiB_copy": r["pct_of_256MiB_copy"],
-                                "best_block_rows": r["config"]["best_block_rows"],
+                                "best_block_rows": r["config"]["best_block_rows"], "best_mode": r["best_mode"],
                                 "h2d_256MiB_GBs": r["h2d_256MiB_GBs"], "lookahead": r["config"]["lookahead"],
                                 "block_rows": r["block_rows"], "mapped": r["mapped"], "resident": r["resident"],
                                 "sha256_y_resident": r["sha256_y_resident"]}

@@ -351,6 +351,67 @@ int qgemv_stream_rows(qg_streamer *st, const qg_matrix *w, int64_t row_start,
 int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_window *win,
                          int32_t n_win, int64_t block_rows, qg_stream_t stream);
 
+/* ---- streamed plans: a layer's streamed steps as one replayed graph ----
+ * neurostream README, "What the numbers taught us": a plan that spans the
+ * layer's projections and experts, instead of one prefetcher per
+ * projection, removed the pipeline drains between them.  A plan is a fixed
+ * list of steps: streamed GEMV steps (windows of pinned host matrices walked
+ * in row blocks through the plan's own ring of lookahead + 1 device slots of
+ * slot_bytes, as qgemv_stream_windows) and elementwise steps between them
+ * (SiLU * up, router-weighted combine).  qgemv_stream_plan_create builds the
+ * whole walk once, as a HIP graph: block b's copy waits only for the kernel
+ * that last read its slot (block b - lookahead - 1), so copies run ahead
+ * across steps while the kernels and elementwise steps run in order.  A run
+ * replays it with one launch, with no per-block host work.  Every kernel is
+ * the qgemv_rows kernel on the ring slot, so every y has the bits of the
+ * resident computation. */
+enum qg_plan_op { QG_PLAN_GEMV = 1, QG_PLAN_SILU_MUL = 2, QG_PLAN_COMBINE = 3 };
+
+typedef struct qg_plan_step {
+  int32_t op;          /* enum qg_plan_op */
+  int32_t fmt;         /* GEMV: format of the step's windows */
+  int64_t k;           /* GEMV: inputs per row */
+  int32_t first_win;   /* GEMV: windows [first_win, first_win + n_win) of the */
+  int32_t n_win;       /*   plan's table; each window belongs to one step */
+  int64_t block_rows;  /* GEMV: rows per streamed block, 0 = whole window */
+  const float *a;      /* SILU_MUL: g;  COMBINE: y, n_sel vectors stride floats apart */
+  const float *b;      /* SILU_MUL: u;  COMBINE: the n_sel weights */
+  float *out;          /* SILU_MUL: h;  COMBINE: out (as qgemv_combine) */
+  int64_t n;           /* SILU_MUL, COMBINE: outputs */
+  int64_t stride;      /* COMBINE: y stride */
+  int32_t n_sel;       /* COMBINE */
+  int32_t reserved;    /* 0 */
+} qg_plan_step;
+
+typedef struct qg_stream_plan qg_stream_plan;
+
+/* Validates the steps against the host window table win (x and y device
+ * pointers; data in pinned host memory, QG_E_NOT_PINNED otherwise; every
+ * block must fit a slot, QG_E_CAPACITY otherwise), allocates the ring and
+ * builds the graph.  Device pointers of the steps and windows are captured:
+ * they must stay valid for the plan's life. */
+int qgemv_stream_plan_create(int64_t slot_bytes, int32_t lookahead, const qg_plan_step *steps,
+                             int32_t n_steps, const qg_window *win, int32_t n_win,
+                             qg_stream_plan **out);
+
+/* Moves streamed window w to rows [row_start, row_start + its length) of the
+ * same host matrix (for example the next token's selected expert); runs
+ * enqueued before the call keep the rows they were enqueued with.
+ * QG_E_RANGE past the matrix's rows; QG_E_ARG for a window no GEMV step
+ * streams. */
+int qgemv_stream_plan_set_rows(qg_stream_plan *p, int32_t w, int64_t row_start);
+
+/* Device bytes of the plan's ring: (lookahead + 1) * slot_bytes. */
+int64_t qgemv_stream_plan_ring_bytes(const qg_stream_plan *p);
+
+/* Enqueues one run of the plan on `stream` (its device must be current).
+ * Runs of one plan share its ring: they must not overlap, so enqueue them
+ * on one stream. */
+int qgemv_stream_plan_run(qg_stream_plan *p, qg_stream_t stream);
+
+/* Waits for the device, frees the plan.  NULL is a no-op. */
+int qgemv_stream_plan_destroy(qg_stream_plan *p);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): qgemv_stream_rows with no
  * streamer and no allocation of any kind.  The ring is a device array of

@@ -54,6 +54,12 @@ class qg_window(ctypes.Structure):
                 ("x", _vp), ("y", _vp)]
 
 
+class qg_plan_step(ctypes.Structure):
+    _fields_ = [("op", _i32), ("fmt", _i32), ("k", _i64), ("first_win", _i32), ("n_win", _i32),
+                ("block_rows", _i64), ("a", _vp), ("b", _vp), ("out", _vp), ("n", _i64), ("stride", _i64),
+                ("n_sel", _i32), ("reserved", _i32)]
+
+
 class qg_chain_window(ctypes.Structure):
     _fields_ = [("data", _vp), ("n_rows", _i64), ("row_start", _i64), ("row_end", _i64),
                 ("x", _vp), ("x2", _vp), ("y", _vp)]
@@ -104,6 +110,12 @@ def lib():
         "qgemv_stream_rows": ([_vp, P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
         "qgemv_stream_windows": ([_vp, _i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
         "qgemv_stream_destroy": ([_vp], ctypes.c_int),
+        "qgemv_stream_plan_create": ([_i64, _i32, P(qg_plan_step), _i32, P(qg_window), _i32, P(_vp)],
+                                     ctypes.c_int),
+        "qgemv_stream_plan_set_rows": ([_vp, _i32, _i64], ctypes.c_int),
+        "qgemv_stream_plan_ring_bytes": ([_vp], _i64),
+        "qgemv_stream_plan_run": ([_vp, _vp], ctypes.c_int),
+        "qgemv_stream_plan_destroy": ([_vp], ctypes.c_int),
         "qgemv_stream_rows_noalloc": ([P(qg_matrix), _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
         "qgemv_mapped_rows": ([P(qg_matrix), _i64, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
         "qgemv_mapped_windows": ([_i32, _i64, P(qg_window), _i32, _i64, _vp], ctypes.c_int),
@@ -413,6 +425,94 @@ class Streamer:
         if getattr(self, "_h", None) is not None and self._h.value:
             h, self._h = self._h, None
             _check(lib().qgemv_stream_destroy(h), "qgemv_stream_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+PLAN_GEMV, PLAN_SILU_MUL, PLAN_COMBINE = 1, 2, 3
+
+
+@dataclass
+class PlanGemv:
+    """A streamed GEMV step of a plan: its windows (same fmt and k; data in
+    pinned host memory) walked in blocks of block_rows."""
+    windows: Sequence[Window]
+    block_rows: int = 0
+
+
+@dataclass
+class PlanSiluMul:
+    """h = silu(g) * u between the steps of a plan."""
+    g: object
+    u: object
+    h: object
+
+
+@dataclass
+class PlanCombine:
+    """out = sum_s w[s] y[s] (as qgemv_combine) between the steps of a plan."""
+    y: object
+    y_stride: int
+    n_sel: int
+    w: object
+    n: int
+    out: object
+
+
+class StreamPlan:
+    """Owner of a qg_stream_plan: a fixed walk of streamed GEMV steps and
+    elementwise steps, replayed by run()."""
+
+    def __init__(self, slot_bytes: int, lookahead: int, steps):
+        wins, cs = [], []
+        for st in steps:
+            if isinstance(st, PlanGemv):
+                first = len(wins)
+                fmt, k = st.windows[0].mat.fmt, st.windows[0].mat.k
+                wins.extend(st.windows)
+                cs.append(qg_plan_step(PLAN_GEMV, int(fmt), int(k), first, len(st.windows), int(st.block_rows),
+                                       None, None, None, 0, 0, 0, 0))
+            elif isinstance(st, PlanSiluMul):
+                n = st.h.numel()
+                cs.append(qg_plan_step(PLAN_SILU_MUL, 0, 0, 0, 0, 0, _f32(st.g, n, "g"), _f32(st.u, n, "u"),
+                                       _f32(st.h, n, "h"), n, 0, 0, 0))
+            elif isinstance(st, PlanCombine):
+                cs.append(qg_plan_step(PLAN_COMBINE, 0, 0, 0, 0, 0, _ptr(st.y), _ptr(st.w), _f32(st.out, st.n, "out"),
+                                       int(st.n), int(st.y_stride), int(st.n_sel), 0))
+            else:
+                raise TypeError(f"not a plan step: {st!r}")
+        sarr = (qg_plan_step * len(cs))(*cs)
+        warr = (qg_window * max(len(wins), 1))(*[w.c() for w in wins])
+        h = _vp()
+        _check(lib().qgemv_stream_plan_create(int(slot_bytes), int(lookahead), sarr, len(cs), warr, len(wins),
+                                              ctypes.byref(h)), "qgemv_stream_plan_create")
+        self._h = h
+        self._keep = list(steps)  # the tensors must outlive the plan
+
+    @property
+    def ring_bytes(self) -> int:
+        return int(lib().qgemv_stream_plan_ring_bytes(self._h))
+
+    def set_rows(self, w: int, row_start: int) -> None:
+        _check(lib().qgemv_stream_plan_set_rows(self._h, int(w), int(row_start)), "qgemv_stream_plan_set_rows")
+
+    def run(self, stream=None) -> None:
+        _check(lib().qgemv_stream_plan_run(self._h, _stream(stream)), "qgemv_stream_plan_run")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            h, self._h = self._h, None
+            _check(lib().qgemv_stream_plan_destroy(h), "qgemv_stream_plan_destroy")
 
     def __enter__(self):
         return self

@@ -908,10 +908,19 @@ GemvFn pick(int32_t fmt, Shape s, int32_t in_op, int32_t out_op) {
 // up[i] the row 0 of window i's up matrix (win.data the gate's; same shape),
 // y[j] = silu(gate_j . x) * (up_j . x); the kernel walks virtual rows, two
 // per output row.
-int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
-                hipStream_t stream, int32_t in_op = QG_IN_X, float eps = 0.0f, int32_t out_op = QG_OUT_Y,
-                const float *const *x2 = nullptr, int nt = 1, int64_t x_stride = 0, int64_t y_stride = 0,
-                const void *const *up = nullptr) {
+// A GEMV launch, prepared: kernel, grid, block and arguments (fn is null for
+// a launch with no rows).
+struct GemvLaunch {
+  GemvFn fn;
+  unsigned grid, block;
+  GemvArgs a;
+};
+
+int prepare_gemv(GemvLaunch *L, int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
+                 int32_t in_op = QG_IN_X, float eps = 0.0f, int32_t out_op = QG_OUT_Y,
+                 const float *const *x2 = nullptr, int nt = 1, int64_t x_stride = 0, int64_t y_stride = 0,
+                 const void *const *up = nullptr) {
+  L->fn = nullptr;
   Shape s;
   int rc = team_shape(fmt, k, &s);
   if (rc) return rc;
@@ -932,7 +941,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
     total += win[n].row_end - win[n].row_start;
     ++n;
   }
-  if (n == 0) return QG_OK;
+  if (n == 0) return QG_OK;  // (L->fn stays null: nothing to launch)
   const int64_t B = block_rows > 0 ? std::min<int64_t>(pm * block_rows, maxlen) : maxlen;
   const int64_t teams_max = std::max<int64_t>(1, (int64_t)device_cus() * gemv_teams_per_cu(fmt, s.wt));
   int tile_rows =
@@ -978,7 +987,21 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
                     : nt == 4 && in_op == QG_IN_X && out_op == QG_OUT_Y ? pick_batch<4>(fmt, s)
                                                                         : nullptr;
   if (!fn) return QG_E_ARG;
-  hipLaunchKernelGGL(fn, dim3((unsigned)teams), dim3(64 * s.wt), 0, stream, a);
+  L->fn = fn;
+  L->grid = (unsigned)teams;
+  L->block = 64u * (unsigned)s.wt;
+  L->a = a;
+  return QG_OK;
+}
+
+int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64_t block_rows,
+                hipStream_t stream, int32_t in_op = QG_IN_X, float eps = 0.0f, int32_t out_op = QG_OUT_Y,
+                const float *const *x2 = nullptr, int nt = 1, int64_t x_stride = 0, int64_t y_stride = 0,
+                const void *const *up = nullptr) {
+  static thread_local GemvLaunch L;  // (4 KB of arguments: kept off the stack)
+  int rc = prepare_gemv(&L, fmt, k, win_in, n_in, block_rows, in_op, eps, out_op, x2, nt, x_stride, y_stride, up);
+  if (rc || !L.fn) return rc;
+  hipLaunchKernelGGL(L.fn, dim3(L.grid), dim3(L.block), 0, stream, L.a);
   QG_HIP(hipGetLastError());
   return QG_OK;
 }
@@ -1505,6 +1528,223 @@ int qgemv_stream_windows(qg_streamer *st, int32_t fmt, int64_t k, const qg_windo
   if (n_win == 0) return QG_OK;
   return stream_windows(st, fmt, k, win, n_win, block_rows, stream);
 }
+
+// ---- streamed plans: a layer's streamed steps as one replayed graph ---------------
+
+}  // extern "C"
+
+struct qg_stream_plan {
+  int device;
+  uint8_t *ring;
+  int64_t slot_bytes, slot_stride;
+  int lookahead;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  // Per plan window: its pinned host matrix, row bytes, rows, current first
+  // row and length; and its copy nodes (node, first row of the block within
+  // the window, bytes, ring destination) for re-pointing.
+  struct Copy {
+    hipGraphNode_t node;
+    int64_t off, bytes;
+    void *dst;
+  };
+  struct Win {
+    const uint8_t *host;
+    int64_t rb, n_rows, row_start, len;
+    bool streamed;
+    std::vector<Copy> copies;
+  };
+  std::vector<Win> wins;
+};
+
+namespace {
+
+int plan_destroy(qg_stream_plan *p) {
+  if (!p) return QG_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (p->exec) (void)hipGraphExecDestroy(p->exec);
+  if (p->graph) (void)hipGraphDestroy(p->graph);
+  if (p->ring) (void)hipFree(p->ring);
+  delete p;
+  return e == hipSuccess ? QG_OK : hip_fail(e, "hipDeviceSynchronize");
+}
+
+int validate_plan(int64_t slot_bytes, int32_t lookahead, const qg_plan_step *steps, int32_t n_steps,
+                  const qg_window *win, int32_t n_win) {
+  if (!steps || (n_win > 0 && !win)) return QG_E_NULL;
+  if (slot_bytes < 1 || lookahead < 1 || lookahead > 64 || n_steps < 1 || n_win < 0) return QG_E_ARG;
+  std::vector<char> used(n_win, 0);
+  for (int i = 0; i < n_steps; ++i) {
+    const qg_plan_step &S = steps[i];
+    int rc;
+    if (S.op == QG_PLAN_GEMV) {
+      if (S.n_win < 1 || S.first_win < 0 || S.first_win > n_win - S.n_win) return QG_E_ARG;
+      if ((rc = validate_windows(S.fmt, S.k, win + S.first_win, S.n_win, S.block_rows))) return rc;
+      const int64_t rb = row_bytes_of(S.fmt, S.k);
+      for (int w = S.first_win; w < S.first_win + S.n_win; ++w) {
+        if (used[w]) return QG_E_ARG;  // a window belongs to one step
+        used[w] = 1;
+        const int64_t len = win[w].row_end - win[w].row_start;
+        if (len == 0) continue;
+        const int64_t B = S.block_rows > 0 ? std::min(S.block_rows, len) : len;
+        if (B * rb > slot_bytes) return QG_E_CAPACITY;
+        if ((rc = check_pinned(win[w].data))) return rc;
+      }
+    } else if (S.op == QG_PLAN_SILU_MUL) {
+      if (S.n < 0) return QG_E_ARG;
+      if (S.n > 0 && (!S.a || !S.b || !S.out)) return QG_E_NULL;
+    } else if (S.op == QG_PLAN_COMBINE) {
+      if (S.n < 0 || S.n_sel < 0 || (S.n_sel > 1 && S.stride < S.n)) return QG_E_ARG;
+      if (S.n > 0 && (!S.out || (S.n_sel > 0 && (!S.a || !S.b)))) return QG_E_NULL;
+    } else {
+      return QG_E_ARG;
+    }
+  }
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_stream_plan_create(int64_t slot_bytes, int32_t lookahead, const qg_plan_step *steps, int32_t n_steps,
+                             const qg_window *win, int32_t n_win, qg_stream_plan **out) {
+  if (!out) return QG_E_NULL;
+  *out = nullptr;
+  int rc = validate_plan(slot_bytes, lookahead, steps, n_steps, win, n_win);
+  if (rc) return rc;
+  qg_stream_plan *p = new qg_stream_plan();
+  p->slot_bytes = slot_bytes;
+  p->slot_stride = (slot_bytes + 255) / 256 * 256;
+  p->lookahead = lookahead;
+  auto fail = [&](int code) {
+    plan_destroy(p);
+    return code;
+  };
+  auto hfail = [&](hipError_t e, const char *what) {
+    int code = hip_fail(e, what);
+    plan_destroy(p);
+    return code;
+  };
+  hipError_t e;
+  if ((e = hipGetDevice(&p->device)) != hipSuccess) return hfail(e, "hipGetDevice");
+  const int nslot = lookahead + 1;
+  if ((e = hipMalloc((void **)&p->ring, (size_t)p->slot_stride * nslot)) != hipSuccess) return hfail(e, "hipMalloc(ring)");
+  if ((e = hipGraphCreate(&p->graph, 0)) != hipSuccess) return hfail(e, "hipGraphCreate");
+  p->wins.resize(n_win);
+  for (int w = 0; w < n_win; ++w) {
+    p->wins[w].host = (const uint8_t *)win[w].data;
+    p->wins[w].n_rows = win[w].n_rows;
+    p->wins[w].row_start = win[w].row_start;
+    p->wins[w].len = win[w].row_end - win[w].row_start;
+    p->wins[w].streamed = false;
+  }
+  // Compute nodes (GEMV blocks, elementwise steps) run in program order, one
+  // after the other; block b's copy waits only for the kernel that last read
+  // its ring slot (block b - lookahead - 1), so copies run ahead across steps.
+  std::vector<hipGraphNode_t> kern;  // kernel node of every streamed block, in order
+  hipGraphNode_t prev = nullptr;     // the last compute node
+  static thread_local GemvLaunch L;
+  for (int i = 0; i < n_steps; ++i) {
+    const qg_plan_step &S = steps[i];
+    if (S.op == QG_PLAN_GEMV) {
+      const int64_t rb = row_bytes_of(S.fmt, S.k);
+      for (int w = S.first_win; w < S.first_win + S.n_win; ++w) {
+        qg_stream_plan::Win &W = p->wins[w];
+        W.rb = rb;
+        W.streamed = true;
+        if (W.len == 0) continue;
+        const int64_t B = S.block_rows > 0 ? std::min(S.block_rows, W.len) : W.len;
+        for (int64_t off = 0; off < W.len; off += B) {
+          const int64_t n = std::min(B, W.len - off);
+          const size_t b = kern.size();
+          uint8_t *dst = p->ring + (int64_t)(b % (size_t)nslot) * p->slot_stride;
+          hipGraphNode_t cn;
+          hipGraphNode_t cdep = b >= (size_t)nslot ? kern[b - nslot] : nullptr;
+          if ((e = hipGraphAddMemcpyNode1D(&cn, p->graph, cdep ? &cdep : nullptr, cdep ? 1 : 0, dst,
+                                           W.host + (W.row_start + off) * rb, (size_t)(n * rb),
+                                           hipMemcpyHostToDevice)) != hipSuccess)
+            return hfail(e, "hipGraphAddMemcpyNode1D");
+          W.copies.push_back({cn, off, n * rb, dst});
+          qg_window blk = {dst, n, 0, n, win[w].x, win[w].y + off};
+          if ((rc = prepare_gemv(&L, S.fmt, S.k, &blk, 1, 0))) return fail(rc);
+          void *args[] = {&L.a};
+          hipKernelNodeParams kp = {};
+          kp.func = (void *)L.fn;
+          kp.gridDim = dim3(L.grid);
+          kp.blockDim = dim3(L.block);
+          kp.sharedMemBytes = 0;
+          kp.kernelParams = args;
+          kp.extra = nullptr;
+          hipGraphNode_t deps[2] = {cn, prev};
+          hipGraphNode_t kn;
+          if ((e = hipGraphAddKernelNode(&kn, p->graph, deps, prev ? 2 : 1, &kp)) != hipSuccess)
+            return hfail(e, "hipGraphAddKernelNode");
+          kern.push_back(kn);
+          prev = kn;
+        }
+      }
+    } else if (S.n > 0 && (S.op == QG_PLAN_SILU_MUL || S.n_sel >= 0)) {
+      const unsigned blocks = (unsigned)std::min<int64_t>((S.n + 255) / 256, 4096);
+      hipKernelNodeParams kp = {};
+      kp.gridDim = dim3(blocks);
+      kp.blockDim = dim3(256);
+      kp.extra = nullptr;
+      const float *a = S.a, *b = S.b;
+      float *o = S.out;
+      int64_t n = S.n, stride = S.stride;
+      int n_sel = S.n_sel;
+      void *sargs[] = {&a, &b, &o, &n};
+      void *cargs[] = {&a, &stride, &n_sel, &b, &n, &o};
+      if (S.op == QG_PLAN_SILU_MUL) {
+        kp.func = (void *)silu_mul_kernel;
+        kp.kernelParams = sargs;
+      } else {
+        kp.func = (void *)combine_kernel;
+        kp.kernelParams = cargs;
+      }
+      hipGraphNode_t kn;
+      if ((e = hipGraphAddKernelNode(&kn, p->graph, prev ? &prev : nullptr, prev ? 1 : 0, &kp)) != hipSuccess)
+        return hfail(e, "hipGraphAddKernelNode");
+      prev = kn;
+    }
+  }
+  if ((e = hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0)) != hipSuccess)
+    return hfail(e, "hipGraphInstantiate");
+  *out = p;
+  return QG_OK;
+}
+
+int qgemv_stream_plan_set_rows(qg_stream_plan *p, int32_t w, int64_t row_start) {
+  if (!p) return QG_E_NULL;
+  if (w < 0 || w >= (int32_t)p->wins.size() || !p->wins[w].streamed) return QG_E_ARG;
+  qg_stream_plan::Win &W = p->wins[w];
+  if (row_start < 0 || row_start + W.len > W.n_rows) return QG_E_RANGE;
+  int dev = 0;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != p->device) return QG_E_ARG;
+  for (const auto &c : W.copies)
+    QG_HIP(hipGraphExecMemcpyNodeSetParams1D(p->exec, c.node, c.dst, W.host + (row_start + c.off) * W.rb,
+                                             (size_t)c.bytes, hipMemcpyHostToDevice));
+  W.row_start = row_start;
+  return QG_OK;
+}
+
+int64_t qgemv_stream_plan_ring_bytes(const qg_stream_plan *p) {
+  if (!p) return QG_E_NULL;
+  return p->slot_bytes * (p->lookahead + 1);
+}
+
+int qgemv_stream_plan_run(qg_stream_plan *p, qg_stream_t stream) {
+  if (!p) return QG_E_NULL;
+  int dev = 0;
+  QG_HIP(hipGetDevice(&dev));
+  if (dev != p->device) return QG_E_ARG;
+  QG_HIP(hipGraphLaunch(p->exec, (hipStream_t)stream));
+  return QG_OK;
+}
+
+int qgemv_stream_plan_destroy(qg_stream_plan *p) { return plan_destroy(p); }
 
 // ---- streaming without allocation -----------------------------------------------
 //

@@ -28,7 +28,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 34, names
+    assert len(names) == 39, names
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -208,6 +208,33 @@ def test_stream_rows_noalloc_validation():
     assert L.qgemv_stream_rows_noalloc(ctypes.byref(mat()), 1, 1, 0, 0, 0, None) == 0  # empty window
     text = open(HEADER).read()
     assert f"#define QG_NOALLOC_RING_BYTES ({q.NOALLOC_RING_BYTES >> 20}ll << 20)" in text
+
+
+def test_stream_plan_validation():
+    L = q.lib()
+    h = ctypes.c_void_p()
+    step = q.qg_plan_step(q.PLAN_GEMV, 1, 64, 0, 1, 0, None, None, None, 0, 0, 0, 0)
+    win = qg_window(FAKE, 8, 0, 8, FAKE, FAKE)
+    S1 = (q.qg_plan_step * 1)(step)
+    W1 = (qg_window * 1)(win)
+    assert L.qgemv_stream_plan_create(1024, 1, S1, 1, W1, 1, None) == E_NULL
+    assert L.qgemv_stream_plan_create(1024, 1, None, 1, W1, 1, ctypes.byref(h)) == E_NULL
+    assert L.qgemv_stream_plan_create(0, 1, S1, 1, W1, 1, ctypes.byref(h)) == E_ARG
+    assert L.qgemv_stream_plan_create(1024, 0, S1, 1, W1, 1, ctypes.byref(h)) == E_ARG
+    assert L.qgemv_stream_plan_create(1024, 1, S1, 0, W1, 1, ctypes.byref(h)) == E_ARG
+    bad = (q.qg_plan_step * 1)(q.qg_plan_step(9, 1, 64, 0, 1, 0, None, None, None, 0, 0, 0, 0))
+    assert L.qgemv_stream_plan_create(1024, 1, bad, 1, W1, 1, ctypes.byref(h)) == E_ARG
+    two = (q.qg_plan_step * 1)(q.qg_plan_step(q.PLAN_GEMV, 1, 64, 0, 2, 0, None, None, None, 0, 0, 0, 0))
+    assert L.qgemv_stream_plan_create(1024, 1, two, 1, W1, 1, ctypes.byref(h)) == E_ARG  # windows past the table
+    nofmt = (q.qg_plan_step * 1)(q.qg_plan_step(q.PLAN_GEMV, 0, 64, 0, 1, 0, None, None, None, 0, 0, 0, 0))
+    assert L.qgemv_stream_plan_create(1024, 1, nofmt, 1, W1, 1, ctypes.byref(h)) == E_FMT
+    silu = (q.qg_plan_step * 1)(q.qg_plan_step(q.PLAN_SILU_MUL, 0, 0, 0, 0, 0, None, FAKE, FAKE, 4, 0, 0, 0))
+    assert L.qgemv_stream_plan_create(1024, 1, silu, 1, W1, 1, ctypes.byref(h)) == E_NULL
+    assert L.qgemv_stream_plan_set_rows(None, 0, 0) == E_NULL
+    assert L.qgemv_stream_plan_run(None, None) == E_NULL
+    assert L.qgemv_stream_plan_ring_bytes(None) == E_NULL
+    assert L.qgemv_stream_plan_destroy(None) == 0
+    assert ctypes.sizeof(q.qg_plan_step) == 80
 
 
 def test_streamer_validation():
