@@ -11,6 +11,7 @@
 
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "qgemv.h"
@@ -686,31 +687,104 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   float xr[C][NT][32];
   float xs[C][NT][2];  // Q4_0, K-quants: the sums of each unit's first and last 16 inputs
   constexpr int in_op = op_in(OP);
-  auto load_x = [&](const float *x, const float *x2) {
+  // A launch's first activations are gathered through the wave's LDS ring
+  // while it is still idle: the column set's 2048 inputs are read 1 KB per
+  // instruction (one cache line per 8 lanes; a lane reading its own 128 bytes
+  // touches 64 lines per instruction, and those loads, not HBM, bounded the
+  // launch's start: 0.2-1.3 us per launch on MI355X), written to LDS with a
+  // rotation inside each 128-byte column, so that the lanes' reads spread over
+  // the banks, and read back by the lane owning each column.  SKB KB per pass,
+  // as much as the ring holds (less with two columns and a SiLU multiplier,
+  // which would otherwise spill registers).  Later windows with other inputs
+  // (copies in flight in the ring) load them directly.
+  constexpr int kRingBytes = NS * SLOT;
+  constexpr int kSkbMax = (op_in(OP) == QG_IN_SILU_MUL && C == 2) ? 2 : 8;  // registers: two columns and x2
+  constexpr int SKB0 = kRingBytes >= 8192 ? 8 : kRingBytes >= 4096 ? 4 : kRingBytes >= 2048 ? 2 : 1;
+  constexpr int SKB = SKB0 < kSkbMax ? SKB0 : kSkbMax;
+  uint8_t *const stg = &ring[wave][0][0];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  // put(q, w): inputs 4q .. 4q + 3 of the lane's column
+  auto gather = [&](const float *src, int c, auto put) {
+    const int base = 32 * (slice_b0 + 64 * c);
+    const int lim = 32 * nb - 4;  // the last 16 bytes of the input vector
+#pragma unroll
+    for (int p = 0; p < 8 / SKB; ++p) {
+      f32x4 v[SKB];
+#pragma unroll
+      for (int i = 0; i < SKB; ++i) {
+        const int f = min(base + 256 * (p * SKB + i) + 4 * lane, lim);
+        __builtin_memcpy(&v[i], src + f, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < SKB; ++i) {
+        const int col = 8 * i + (lane >> 3);
+        *reinterpret_cast<f32x4 *>(stg + 128 * col + 16 * (((lane & 7) + col) & 7)) = v[i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const int cl = lane - 8 * SKB * p;
+      if (cl >= 0 && cl < 8 * SKB) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) put(q, *reinterpret_cast<const f32x4 *>(stg + 128 * cl + 16 * ((q + cl) & 7)));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+  };
+  auto load_x_staged = [&](const float *x, const float *x2) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int j = slice_b0 + lane + 64 * c;
-      const int jj = min(j, nb - 1);
+      const bool ok = j < nb;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float *xt = NT == 1 ? x : x + t * a.x_stride;
+        gather(xt, c, [&](int q, f32x4 w) {
+          xr[c][t][4 * q + 0] = w.x;
+          xr[c][t][4 * q + 1] = w.y;
+          xr[c][t][4 * q + 2] = w.z;
+          xr[c][t][4 * q + 3] = w.w;
+        });
+        if constexpr (in_op == QG_IN_SILU_MUL) {
+          gather(x2, c, [&](int q, f32x4 u) {
+            xr[c][t][4 * q + 0] = silu_times(xr[c][t][4 * q + 0], u.x);
+            xr[c][t][4 * q + 1] = silu_times(xr[c][t][4 * q + 1], u.y);
+            xr[c][t][4 * q + 2] = silu_times(xr[c][t][4 * q + 2], u.z);
+            xr[c][t][4 * q + 3] = silu_times(xr[c][t][4 * q + 3], u.w);
+          });
+        }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          float4 v;
-          __builtin_memcpy(&v, xt + 32 * jj + 4 * q, 16);
-          if constexpr (in_op == QG_IN_SILU_MUL) {
-            float4 u;
-            __builtin_memcpy(&u, x2 + 32 * jj + 4 * q, 16);
-            v.x = silu_times(v.x, u.x);
-            v.y = silu_times(v.y, u.y);
-            v.z = silu_times(v.z, u.z);
-            v.w = silu_times(v.w, u.w);
+        for (int e = 0; e < 32; ++e) xr[c][t][e] = ok ? xr[c][t][e] : 0.0f;
+      }
+    }
+  };
+  auto load_x = [&](const float *x, const float *x2, auto staged) {
+    if constexpr (decltype(staged)::value) {
+      load_x_staged(x, x2);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = slice_b0 + lane + 64 * c;
+        const int jj = min(j, nb - 1);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float *xt = NT == 1 ? x : x + t * a.x_stride;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            float4 v;
+            __builtin_memcpy(&v, xt + 32 * jj + 4 * q, 16);
+            if constexpr (in_op == QG_IN_SILU_MUL) {
+              float4 u;
+              __builtin_memcpy(&u, x2 + 32 * jj + 4 * q, 16);
+              v.x = silu_times(v.x, u.x);
+              v.y = silu_times(v.y, u.y);
+              v.z = silu_times(v.z, u.z);
+              v.w = silu_times(v.w, u.w);
+            }
+            const bool ok = j < nb;
+            xr[c][t][4 * q + 0] = ok ? v.x : 0.0f;
+            xr[c][t][4 * q + 1] = ok ? v.y : 0.0f;
+            xr[c][t][4 * q + 2] = ok ? v.z : 0.0f;
+            xr[c][t][4 * q + 3] = ok ? v.w : 0.0f;
           }
-          const bool ok = j < nb;
-          xr[c][t][4 * q + 0] = ok ? v.x : 0.0f;
-          xr[c][t][4 * q + 1] = ok ? v.y : 0.0f;
-          xr[c][t][4 * q + 2] = ok ? v.z : 0.0f;
-          xr[c][t][4 * q + 3] = ok ? v.w : 0.0f;
         }
       }
     }
@@ -794,7 +868,9 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       f_end = true;
     }
   };
-  load_x(CW.x, CW.x2);  // before the ring's first copies: its wait then drains nothing else
+  // before the ring's first copies: the loads' wait then drains nothing else
+  load_x(CW.x, CW.x2, std::true_type{});
+  wait_lds_reads();  // the gather's reads of the ring are done before copies land in it
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
     issue(fp, s);
@@ -808,7 +884,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   int parity = 0;
   for (;;) {
     if (CW.x != cx || (in_op == QG_IN_SILU_MUL && CW.x2 != cx2)) {
-      load_x(CW.x, CW.x2);
+      load_x(CW.x, CW.x2, std::false_type{});
       cx = CW.x;
       cx2 = CW.x2;
     }
