@@ -525,16 +525,18 @@ template <int FMT, int C> struct Geo {
 
 // Concurrency of gemv_kernel, a function of (format, team size): Q8_0 runs
 // about six waves per compute unit, each with two rows in flight while it
-// computes one more; the 4-bit formats, with twice the decode work per byte,
-// run twelve waves with one row in flight.  More requests in flight than that
-// (more waves, deeper rings) made the same walks slower on MI355X: HBM serves
-// a compact, moderate stream better than a wide, deep one.
+// computes one more (one row in flight in teams of more than six waves); the
+// 4-bit and 6-bit formats, with more decode work per byte, run twelve waves,
+// each with two rows in flight.  More requests in flight than that (more
+// waves, deeper rings, or two rows in Q8_0's twelve-wave teams) made the same
+// walks slower on MI355X: HBM serves a compact, moderate stream better than a
+// wide, deep one.
 __host__ __device__ constexpr int gemv_waves_per_cu(int fmt) { return fmt == QG_Q8_0 ? 6 : 12; }
 __host__ __device__ constexpr int gemv_teams_per_cu(int fmt, int wt) {
   return wt >= gemv_waves_per_cu(fmt) ? 1 : gemv_waves_per_cu(fmt) / wt;
 }
 __host__ __device__ constexpr int gemv_in_flight(int fmt, int wt) {
-  return fmt == QG_Q8_0 && wt * gemv_teams_per_cu(fmt, wt) <= 6 ? 2 : 1;
+  return fmt != QG_Q8_0 || wt * gemv_teams_per_cu(fmt, wt) <= 6 ? 2 : 1;
 }
 constexpr int kGemvTileRows = 8;  // most rows per tile
 
