@@ -30,6 +30,9 @@ HIPCC_FLAGS = [
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first three kernel arguments of every kernel arrive in scalar
+    # registers (the GEMV kernels' leading x, nb and tile count)
+    "-mllvm", "-amdgpu-kernarg-preload-count=3",
 ]
 
 

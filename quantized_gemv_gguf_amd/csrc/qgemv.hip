@@ -1001,7 +1001,7 @@ int launch_gemv(int32_t fmt, int64_t k, const qg_window *win_in, int n_in, int64
   static thread_local GemvLaunch L;  // (4 KB of arguments: kept off the stack)
   int rc = prepare_gemv(&L, fmt, k, win_in, n_in, block_rows, in_op, eps, out_op, x2, nt, x_stride, y_stride, up);
   if (rc || !L.fn) return rc;
-  hipLaunchKernelGGL(L.fn, dim3(L.grid), dim3(L.block), 0, stream, L.a);
+  hipLaunchKernelGGL(L.fn, dim3(L.grid), dim3(L.block), 0, stream, L.a.win[0].x, L.a.nb, L.a.n_tiles, L.a);
   QG_HIP(hipGetLastError());
   return QG_OK;
 }
@@ -1668,7 +1668,9 @@ int qgemv_stream_plan_create(int64_t slot_bytes, int32_t lookahead, const qg_pla
           W.copies.push_back({cn, off, n * rb, dst});
           qg_window blk = {dst, n, 0, n, win[w].x, win[w].y + off};
           if ((rc = prepare_gemv(&L, S.fmt, S.k, &blk, 1, 0))) return fail(rc);
-          void *args[] = {&L.a};
+          const float *x_first = L.a.win[0].x;
+          int32_t nb_first = L.a.nb, tiles_first = L.a.n_tiles;
+          void *args[] = {&x_first, &nb_first, &tiles_first, &L.a};
           hipKernelNodeParams kp = {};
           kp.func = (void *)L.fn;
           kp.gridDim = dim3(L.grid);

@@ -584,7 +584,8 @@ __host__ __device__ constexpr bool op_pair(int op) { return op == kOpSwiglu || o
 // decoded once and dotted with each token's activations, in the one-token
 // order, so each token's y has the bits of a one-token launch.
 template <int FMT, int WT, int C, int OP, int NT = 1>
-__global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
+__global__ void __launch_bounds__(64 * WT) gemv_kernel(const float *x_first, int32_t nb_first, int32_t tiles_first,
+                                                       const GemvArgs a) {
   static_assert(NT == 1 || OP == kOpNone, "fused transforms take one token");
   static_assert(!op_pair(OP) || kGemvTileRows % 2 == 0, "SwiGLU tiles hold whole pairs");
   using G = Geo<FMT, C>;
@@ -706,6 +707,14 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   uint8_t *const stg = &ring[wave][0][0];
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   // put(q, w): inputs 4q .. 4q + 3 of the lane's column
+  // The first pass of the first window's gather is issued before the kernel
+  // reads its argument block: the launch passes that window's x, nb and the
+  // tile count as leading arguments, which the library's build preloads into
+  // scalar registers (gfx950 kernel-argument preloading), so the loads go out
+  // at the wave's first instructions instead of after a round trip to the
+  // argument block in device memory.
+  f32x4 pre[SKB];
+  bool use_pre = false;
   auto gather = [&](const float *src, int c, auto put) {
     const int base = 32 * (slice_b0 + 64 * c);
     const int lim = 32 * nb - 4;  // the last 16 bytes of the input vector
@@ -714,8 +723,12 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
       f32x4 v[SKB];
 #pragma unroll
       for (int i = 0; i < SKB; ++i) {
-        const int f = min(base + 256 * (p * SKB + i) + 4 * lane, lim);
-        __builtin_memcpy(&v[i], src + f, 16);
+        if (p == 0 && c == 0 && use_pre) {
+          v[i] = pre[i];
+        } else {
+          const int f = min(base + 256 * (p * SKB + i) + 4 * lane, lim);
+          __builtin_memcpy(&v[i], src + f, 16);
+        }
       }
 #pragma unroll
       for (int i = 0; i < SKB; ++i) {
@@ -837,11 +850,21 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
   // Past the team's last row the cursor stays on that row, re-copying it into
   // a slot no computation reads, which keeps one fixed count of loads per row.
   Win CW, FW;
+  if ((int)blockIdx.x >= tiles_first) return;
+  constexpr bool kPre = NT == 1 && op_in(OP) != QG_IN_SILU_MUL;
+  if constexpr (kPre) {
+    const int lim = 32 * nb_first - 4;
+#pragma unroll
+    for (int i = 0; i < SKB; ++i) {
+      const int f = min(32 * slice_b0 + 256 * i + 4 * lane, lim);
+      __builtin_memcpy(&pre[i], x_first + f, 16);
+    }
+  }
   load_win(0, CW);
   // An empty statement consuming those fields keeps the compiler from
   // sinking their loads past the branches below (one wait, not four).
   asm volatile("" ::"s"(n_tiles), "s"(B), "s"(TR), "s"(tpb), "s"(eps), "s"(T), "s"(CW.t0), "s"(CW.t1),
-               "s"(CW.row_start), "s"(CW.row_end), "s"(CW.base), "s"(CW.x), "s"(CW.x2), "s"(CW.y));
+               "s"(CW.row_start), "s"(CW.row_end), "s"(CW.base), "s"(CW.x), "s"(CW.x2), "s"(CW.y) : "memory");
   if ((int)blockIdx.x >= n_tiles) return;
   Tile cur, F;
   locate(blockIdx.x, CW, cur);
@@ -871,7 +894,9 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
     }
   };
   // before the ring's first copies: the loads' wait then drains nothing else
+  use_pre = kPre && CW.x == x_first;
   load_x(CW.x, CW.x2, std::true_type{});
+  use_pre = false;
   wait_lds_reads();  // the gather's reads of the ring are done before copies land in it
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
@@ -1002,7 +1027,7 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const GemvArgs a) {
 // Team shape (WT waves, C block columns per lane), a function of (format, k).
 struct Shape { int wt, c; };
 
-typedef void (*GemvFn)(GemvArgs);
+typedef void (*GemvFn)(const float *, int32_t, int32_t, GemvArgs);
 
 template <int FMT, int C, int OP, int... WT>
 GemvFn pick_wt(int wt, std::integer_sequence<int, WT...>) {
