@@ -284,16 +284,44 @@ template <> struct Fmt<QG_Q4_K> {
 // (q = 32) adds exactly zero and the dot takes no sum of x.  The factor 4
 // comes out of d exactly.  The dequant kernel forms the weights from the same
 // codes().
+// N words of LDS starting at byte p (any alignment), read as N + 1 aligned
+// dwords and funnel-shifted into place (p must point into LDS; the reads may
+// touch up to 3 bytes past the last word, which the staged rows leave room
+// for).  gfx950 serves unaligned DS reads, but each one stalls the CU's LDS
+// pipe (SQ_LDS_UNALIGNED_STALL): for Q6_K's 210-byte super-blocks, whose
+// alignment changes from one to the next, those stalls bounded the kernel
+// (the Q4_K_M pass's Q6_K down projection 40.1 -> 27.0 us per launch with
+// this), and for MXFP4's 17-byte blocks they cost the MoE grids a little.
+// For Q8_0 and Q4_0 the extra shifts cost more than the stalls.
+template <int N>
+__device__ __forceinline__ void lds_words(const uint8_t *p, uint32_t (&q)[N]) {
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+  lds_u8 *lp = (lds_u8 *)p;
+  const uint32_t mis = (uint32_t)(uintptr_t)lp & 3u;
+  lds_u32 *w = (lds_u32 *)(lp - mis);
+  uint32_t v[N + 1];
+#pragma unroll
+  for (int i = 0; i <= N; ++i) v[i] = w[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) q[i] = __builtin_amdgcn_alignbit(v[i + 1], v[i], 8 * mis);
+}
+
 template <> struct Fmt<QG_Q6_K> {
   static constexpr int kBytes = 210, kUnits = 8;
   static constexpr bool kSums = false, kDot = true;
   // Byte l of word w of q is 4 (q_e - 32) for element e = 4 w + l of unit u.
-  template <typename P>
-  __device__ static inline void codes(const P *blk, int u, uint32_t q[8]) {
+  template <bool kLds>
+  __device__ static inline void codes(const uint8_t *blk, int u, uint32_t q[8]) {
     const int h = u >> 2, i = u & 3;
     uint32_t lo[8], hi[8];
-    __builtin_memcpy(lo, blk + 64 * h + 32 * (i & 1), 32);
-    __builtin_memcpy(hi, blk + 128 + 32 * h, 32);
+    if constexpr (kLds) {
+      lds_words<8>(blk + 64 * h + 32 * (i & 1), lo);
+      lds_words<8>(blk + 128 + 32 * h, hi);
+    } else {
+      __builtin_memcpy(lo, blk + 64 * h + 32 * (i & 1), 32);
+      __builtin_memcpy(hi, blk + 128 + 32 * h, 32);
+    }
     // rotations right: the nibble at bit 4 (i >= 2) or 0 of each byte to bit
     // 2; bits 2 i, 2 i + 1 to bits 6, 7 (bits that wrap into another byte land
     // outside the kept field)
@@ -307,7 +335,7 @@ template <> struct Fmt<QG_Q6_K> {
   __device__ static inline void dot(const uint8_t *blk, int u, const float (&x)[NT][32], const float (&)[NT][2],
                                     const float (&acc)[NT], float (&res)[NT]) {
     uint32_t q[8];
-    codes(blk, u, q);
+    codes<true>(blk, u, q);
     const float sa = (float)(int8_t)blk[192 + 2 * u], sb = (float)(int8_t)blk[193 + 2 * u];
     uint32_t hd = 0;
     __builtin_memcpy(&hd, blk + 208, 2);
@@ -326,7 +354,7 @@ template <> struct Fmt<QG_Q6_K> {
   // The 32 weights of unit u, each rounded once: d scale is exact in fp32.
   __device__ static inline void dequant(const uint8_t *blk, int u, float w[32]) {
     uint32_t q[8];
-    codes(blk, u, q);
+    codes<false>(blk, u, q);
     uint32_t hd = 0;
     __builtin_memcpy(&hd, blk + 208, 2);
     const float d4 = half_bits(hd) * 0.25f;
@@ -452,11 +480,15 @@ __device__ __forceinline__ void row_partial(const uint8_t *sb, int ph, int lane,
     for (int c = 0; c < C; ++c) {
       const int b = lane + 64 * c;
       const int bo = ph + F::kBytes * b;  // block's byte offset in the staged row
-      // LDS reads at any byte alignment (gfx950 serves unaligned DS accesses):
-      // the payload needs no realignment in registers.
+      // LDS reads at any byte alignment (gfx950 serves unaligned DS accesses;
+      // MXFP4 realigns aligned words instead, as above).
       uint32_t sbits = 0, q[F::kWords];
       __builtin_memcpy(&sbits, sb + bo, F::kScaleBytes);
-      __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
+      if constexpr (FMT == QG_MXFP4) {
+        lds_words<F::kWords>(sb + bo + F::kScaleBytes, q);
+      } else {
+        __builtin_memcpy(q, sb + bo + F::kScaleBytes, 4 * F::kWords);
+      }
       float u[32];
       F::decode(q, u);
 #pragma unroll
