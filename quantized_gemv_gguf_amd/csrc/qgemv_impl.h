@@ -894,7 +894,8 @@ __global__ void __launch_bounds__(64 * WT) gemv_kernel(const float *x_first, int
   }
   load_win(0, CW);
   // An empty statement consuming those fields keeps the compiler from
-  // sinking their loads past the branches below (one wait, not four).
+  // sinking their loads past the branches below (one wait, not four); its
+  // memory clobber keeps the activation prefetch above it.
   asm volatile("" ::"s"(n_tiles), "s"(B), "s"(TR), "s"(tpb), "s"(eps), "s"(T), "s"(CW.t0), "s"(CW.t1),
                "s"(CW.row_start), "s"(CW.row_end), "s"(CW.base), "s"(CW.x), "s"(CW.x2), "s"(CW.y) : "memory");
   if ((int)blockIdx.x >= n_tiles) return;
