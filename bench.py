@@ -725,12 +725,14 @@ def q4_0_workload(args, dev):
     L = q.lib()
     st = torch.cuda.current_stream().cuda_stream
     cm = [q.qg_matrix(m.data_ptr(), q.Q4_0, 0, rows, k, nbytes) for m in mats]
+    # arguments marshalled once (a tensor view per call costs the host a few µs)
+    cmr = [ctypes.byref(m) for m in cm]
+    xp, y0p = x.data_ptr(), ys[0].data_ptr()
 
     def one(i, B=0):
-        rc = L.qgemv_rows(ctypes.byref(cm[i % ncopy]), 0, rows, x.data_ptr(), ys[0].data_ptr(), B, st)
+        rc = L.qgemv_rows(cmr[i % ncopy], 0, rows, xp, y0p, B, st)
         assert rc == 0
 
-    wins = [q.Window(q.Matrix(mats[j], q.Q4_0, rows, k), 0, rows, x, ys[j]) for j in range(16)]
     arrs = []
     for g in range(ncopy // 16):
         ws = [q.Window(q.Matrix(mats[16 * g + j], q.Q4_0, rows, k), 0, rows, x, ys[j]) for j in range(16)]
@@ -791,26 +793,29 @@ def moe_workload(args, dev):
     mats = [q.Matrix(torch.from_numpy(h).to(dev), q.MXFP4, rows, k) for h in host]
     ids = synth.expert_ids(E, ns, c["tokens"], synth.seed_of(4, 8))
     xs = torch.from_numpy(np.stack([synth.x_vec(k, synth.seed_of(4, 100 + t)) for t in range(c["tokens"])])).to(dev)
-    gu = torch.empty(2 * ns * out, dtype=torch.float32, device=dev)
     h = torch.empty(ns * out, dtype=torch.float32, device=dev)
     ye = torch.empty(ns * out, dtype=torch.float32, device=dev)
     y = torch.empty((c["tokens"], out), dtype=torch.float32, device=dev)
     wts = torch.from_numpy(synth.router_weights(c["tokens"], ns, synth.seed_of(4, 9))).to(dev)
     L = q.lib()
     st = torch.cuda.current_stream().cuda_stream
-    m2 = (q.qg_matrix * 2)(mats[0].c(), mats[1].c())
     m1 = (q.qg_matrix * 1)(mats[2].c())
     gate_c, up_c = mats[0].c(), mats[1].c()
     gate_m, up_m = ctypes.byref(gate_c), ctypes.byref(up_c)
     idarr = [(ctypes.c_int32 * ns)(*[int(v) for v in ids[t]]) for t in range(c["tokens"])]
+    # device addresses taken once: a tensor view per call costs the host a few
+    # µs, which is marshalling, not the path
+    xp = [xs[t].data_ptr() for t in range(c["tokens"])]
+    wp = [wts[t].data_ptr() for t in range(c["tokens"])]
+    yp = [y[t].data_ptr() for t in range(c["tokens"])]
+    hp, yep = h.data_ptr(), ye.data_ptr()
     B = args.block_rows
 
     def token(t):
         t = t % c["tokens"]
-        rc = L.qgemv_expert_swiglu(gate_m, up_m, E, idarr[t], ns, xs[t].data_ptr(), 0, q.IN_X, 0.0, h.data_ptr(),
-                                   B, st)
-        rc |= L.qgemv_expert_windows(m1, 1, E, idarr[t], ns, h.data_ptr(), out, ye.data_ptr(), B, st)
-        rc |= L.qgemv_combine(ye.data_ptr(), out, ns, wts[t].data_ptr(), out, y[t].data_ptr(), st)
+        rc = L.qgemv_expert_swiglu(gate_m, up_m, E, idarr[t], ns, xp[t], 0, q.IN_X, 0.0, hp, B, st)
+        rc |= L.qgemv_expert_windows(m1, 1, E, idarr[t], ns, hp, out, yep, B, st)
+        rc |= L.qgemv_combine(yep, out, ns, wp[t], out, yp[t], st)
         assert rc == 0
 
     for t in range(args.warmup):
@@ -1103,9 +1108,10 @@ def q8_0_small_workload(args, dev):
     L = q.lib()
     st = torch.cuda.current_stream().cuda_stream
     m = q.Matrix(w, q.Q8_0, rows, k).c()
+    mr, xp, yp = ctypes.byref(m), x.data_ptr(), y.data_ptr()
 
     def one(i):
-        assert L.qgemv_rows(ctypes.byref(m), 0, rows, x.data_ptr(), y.data_ptr(), 0, st) == 0
+        assert L.qgemv_rows(mr, 0, rows, xp, yp, 0, st) == 0
 
     for i in range(10):
         one(i)
