@@ -86,8 +86,8 @@ def profiled_traffic(kernel: str):
 
 def threads() -> int:
     """Host threads for the oracle and the generators: every CPU this process
-    may run on, capped by OMP_NUM_THREADS where the host sets it (a GPU machine
-    gives each GPU a share of its cores that way)."""
+    may run on, capped by OMP_NUM_THREADS where the host sets it (a host
+    shared by several GPUs may give each its share of the cores that way)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
@@ -1294,8 +1294,9 @@ def main(argv=None):
                    help="first run a 256 MiB device-to-device copy (a kernel of known traffic, to scale HBM counters)")
     args = p.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU split is a design note, not built)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(splitting the rows over several GPUs is described in the design notes, not implemented)",
+              file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
