@@ -50,9 +50,12 @@
  *    every stream.  Pointers marked "device" are device (HBM) addresses; the
  *    streamed entry points take weights in page-locked host memory
  *    (hipHostMalloc / pinned), checked, never pageable.
- *  - Asynchrony: compute entry points enqueue on `stream` (NULL = the default
- *    stream) and return without waiting.  Only qgemv_stream_create and
- *    qgemv_stream_destroy synchronise.
+ *  - Asynchrony: compute entry points (the GEMVs, the elementwise steps,
+ *    qgemv_stream_rows / _windows / _rows_noalloc, qgemv_stream_plan_run and
+ *    qgemv_chain_run) enqueue on `stream` (NULL = the default stream) and
+ *    return without waiting.  qgemv_stream_create / _destroy,
+ *    qgemv_stream_plan_destroy and qgemv_chain_create / _check /
+ *    _set_spin_limit / _destroy wait for the device.
  *  - Outputs: y receives exactly row_end - row_start values; nothing outside
  *    that range is written.
  *  - Determinism: a row's result depends only on its own bytes, x, the format
