@@ -155,8 +155,6 @@ int64_t qgemv_weight_bytes(int32_t fmt, int64_t n_rows, int64_t k);
 int qgemv_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
                const float *x, float *y, int64_t block_rows, qg_stream_t stream);
 
-/* Input transforms (qgemv_rows_op, chain steps) and output transforms
- * (qgemv_rows_op). */
 /* A small batch: y_t = W[row_start:row_end] . x_t for n_tok tokens t, with
  * every weight block read from memory and decoded once per pass for several
  * tokens (neurostream README, "What the numbers taught us": tokens that share
@@ -190,6 +188,8 @@ int qgemv_rows_mfma(const qg_matrix *w, int64_t row_start, int64_t row_end,
                     const float *x, int64_t x_stride, int32_t n_tok, float *y,
                     int64_t y_stride, qg_stream_t stream);
 
+/* Input transforms (qgemv_rows_op, chain steps) and output transforms
+ * (qgemv_rows_op). */
 enum qg_in_op { QG_IN_X = 0, QG_IN_RMS = 1, QG_IN_GELU_RMS = 2, QG_IN_SILU_MUL = 3 };
 enum qg_out_op { QG_OUT_Y = 0, QG_OUT_GELU = 1 };
 
@@ -321,8 +321,8 @@ int qgemv_dequant_rows(const qg_matrix *w, int64_t row_start, int64_t row_end,
                        float *out, qg_stream_t stream);
 
 /* ---- streamed weights: pinned host memory -> device ring -> same kernels ----
- * A streamer owns lookahead + 1 device slots of slot_bytes each, one copy
- * stream and per-slot events (neurostream README, "The idea": blocks sized so
+ * A streamer owns lookahead + 1 device slots of slot_bytes each and per-slot
+ * events (neurostream README, "The idea": blocks sized so
  * that lookahead + 1 buffers fit; "Bugs worth knowing about": the pipeline
  * holds depth + 1 blocks, because the block being multiplied keeps its
  * buffer until its output exists).  Block k is copied into slot
