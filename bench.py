@@ -367,6 +367,17 @@ def dense_workload(args, dev, cfg=5):
     wall = time.perf_counter() - t0
     gpu_ms = g0.elapsed_time(g1)
     d_end = model.d.clone()
+    eager = None
+    if graph is not None:
+        # the same number of tokens issued from the host, right after, for
+        # comparison (timing only: the parity replay below starts from d_start)
+        torch.cuda.synchronize()
+        t0e = time.perf_counter()
+        for s in range(args.steps):
+            model.token_fused()
+        torch.cuda.synchronize()
+        we = time.perf_counter() - t0e
+        eager = {"value": model.bytes_per_token * args.steps / we / 1e9, "ms_per_step": we / args.steps * 1e3}
     # per-kernel durations: right after the timed region, each kernel variant's
     # launches of two tokens run back to back on the launch stream, bracketed by
     # one pair of HIP events (an event pair around every single launch would
@@ -409,6 +420,8 @@ def dense_workload(args, dev, cfg=5):
         "kernels": kernels,
         "sha256_final_carry": sha256_of(d_end),
     }
+    if eager is not None:
+        res["eager_launches"] = eager
     # identity: tokens/s = bandwidth / active bytes per token
     assert abs(res["tokens_per_s"] - gbs * 1e9 / model.bytes_per_token) <= 1e-9 * res["tokens_per_s"]
     if not args.no_check:
